@@ -1,0 +1,689 @@
+// api.cpp -- host runtime behind the C ABI in include/dfa.h: argument
+// validation, work planning over a block list, workspace layout and kernel
+// launches on the caller's stream.
+//
+// Planning.  A block list is regrouped two ways:
+//  * by query piece (q_start, len_q, stride): each piece keeps its blocks in
+//    ring-step order -- the order in which a virtual rank receives key/value
+//    shards -- and is cut into query tiles (forward, dQ);
+//  * by key piece (kv_start, len_kv, stride): each keeps the blocks that read
+//    it, again in step order, cut into key tiles (dK, dV).
+// Work tiles are sorted by decreasing cost so the heaviest start first.  The
+// tables travel to the device in the caller's workspace; the kernels read
+// key/value rows of the owning rank in place, so a ring step costs no copy
+// (the buffer hand-off of the DistFlashAttn Guide, "Core Innovation 2").
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <tuple>
+#include <vector>
+
+#include "dfa.h"
+#include "dfa_internal.h"
+
+namespace {
+
+using dfa::KvRef;
+using dfa::KvSeg;
+using dfa::MergeItem;
+using dfa::QRef;
+using dfa::QSeg;
+using dfa::Tile;
+
+constexpr size_t kAlign = 256;
+constexpr int kCostTileKV = 64;  // granularity of the cost estimate
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int64_t floor_div(int64_t a, int64_t b) {
+  int64_t q = a / b;
+  if ((a % b != 0) && ((a < 0) != (b < 0))) --q;
+  return q;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+dfa_status check_desc(const dfa_attn_desc *d) {
+  if (!d) return DFA_E_NULL;
+  if (d->dtype != DFA_BF16 && d->dtype != DFA_F32) return DFA_E_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return DFA_E_UNSUPPORTED;
+  if (d->batch < 1 || d->heads_q < 1 || d->heads_kv < 1 || d->seqlen < 1) return DFA_E_SHAPE;
+  if (d->heads_q % d->heads_kv) return DFA_E_SHAPE;
+  if (!std::isfinite(d->softmax_scale)) return DFA_E_SHAPE;
+  const int64_t elems16 = d->dtype == DFA_BF16 ? 8 : 4;  // elements per 16 bytes
+  const int64_t *all[4] = {d->q_strides, d->k_strides, d->v_strides, d->o_strides};
+  for (auto s : all)
+    for (int i = 0; i < 3; ++i) {
+      if (s[i] < 0) return DFA_E_SHAPE;
+      if (s[i] % elems16) return DFA_E_ALIGN;
+    }
+  return DFA_OK;
+}
+
+bool ptr_aligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+dfa_status check_block(const dfa_attn_desc *d, const dfa_block &b) {
+  const int64_t N = d->seqlen;
+  if (b.len_q < 1 || b.len_kv < 1 || b.stride < 1) return DFA_E_SHAPE;
+  if (b.q_start < 0 || b.kv_start < 0) return DFA_E_SHAPE;
+  if (b.q_start > N - 1 || (b.len_q - 1) > (N - 1 - b.q_start) / b.stride) return DFA_E_SHAPE;
+  if (b.kv_start > N - 1 || (b.len_kv - 1) > (N - 1 - b.kv_start) / b.stride) return DFA_E_SHAPE;
+  // the block's mask must be the global-position rule
+  if (b.diag_offset != floor_div(b.q_start - b.kv_start, b.stride)) return DFA_E_SHAPE;
+  return DFA_OK;
+}
+
+using PieceKey = std::tuple<int64_t, int64_t, int64_t>;  // start, len, stride
+
+// Distinct pieces must not share rows.  Returns false on overlap; sets
+// `full` when the pieces cover every position.
+bool pieces_disjoint(const std::vector<PieceKey> &pieces, int64_t N, bool &full) {
+  std::vector<uint8_t> seen(static_cast<size_t>(N), 0);
+  int64_t covered = 0;
+  for (const auto &p : pieces) {
+    const int64_t s = std::get<0>(p), len = std::get<1>(p), st = std::get<2>(p);
+    for (int64_t i = 0; i < len; ++i) {
+      uint8_t &x = seen[static_cast<size_t>(s + i * st)];
+      if (x) return false;
+      x = 1;
+    }
+    covered += len;
+  }
+  full = covered == N;
+  return true;
+}
+
+// ---- query-major plan (forward, dQ) ----
+struct QPlan {
+  std::vector<QSeg> segs;
+  std::vector<KvRef> kv;
+  std::vector<Tile> tiles;
+  bool full = false;
+};
+
+dfa_status plan_q(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n, int tileq,
+                  QPlan &out) {
+  std::map<PieceKey, std::vector<int64_t>> by_piece;
+  std::vector<PieceKey> order;
+  for (int64_t i = 0; i < n; ++i) {
+    const dfa_block &b = blocks[i];
+    PieceKey key{b.q_start, b.len_q, b.stride};
+    auto it = by_piece.find(key);
+    if (it == by_piece.end()) {
+      order.push_back(key);
+      by_piece[key] = {i};
+    } else {
+      it->second.push_back(i);
+    }
+  }
+  if (!pieces_disjoint(order, d->seqlen, out.full)) return DFA_E_SHAPE;
+  struct Cost {
+    int64_t cost;
+    Tile t;
+  };
+  std::vector<Cost> costs;
+  for (const auto &key : order) {
+    auto idx = by_piece[key];
+    std::stable_sort(idx.begin(), idx.end(), [&](int64_t a, int64_t b) {
+      return std::make_tuple(blocks[a].step, blocks[a].kv_start) <
+             std::make_tuple(blocks[b].step, blocks[b].kv_start);
+    });
+    QSeg s{};
+    s.q_start = std::get<0>(key);
+    s.len_q = std::get<1>(key);
+    s.stride = std::get<2>(key);
+    s.part_off = 0;
+    s.blk_begin = static_cast<int32_t>(out.kv.size());
+    s.blk_count = static_cast<int32_t>(idx.size());
+    for (int64_t bi : idx) {
+      if (blocks[bi].stride != s.stride) return DFA_E_SHAPE;
+      out.kv.push_back(KvRef{blocks[bi].kv_start, blocks[bi].len_kv, blocks[bi].diag_offset});
+    }
+    const int32_t seg_id = static_cast<int32_t>(out.segs.size());
+    out.segs.push_back(s);
+    const int64_t nt = ceil_div(s.len_q, tileq);
+    for (int64_t t = 0; t < nt; ++t) {
+      const int64_t iend = std::min<int64_t>((t + 1) * tileq, s.len_q);
+      int64_t c = 0;
+      for (int64_t bi : idx) {
+        const int64_t hi = std::min<int64_t>(blocks[bi].len_kv, iend + blocks[bi].diag_offset);
+        if (hi > 0) c += ceil_div(hi, kCostTileKV);
+      }
+      costs.push_back(Cost{c, Tile{seg_id, static_cast<int32_t>(t)}});
+    }
+  }
+  std::stable_sort(costs.begin(), costs.end(),
+                   [](const Cost &a, const Cost &b) { return a.cost > b.cost; });
+  out.tiles.reserve(costs.size());
+  for (const auto &c : costs) out.tiles.push_back(c.t);
+  return DFA_OK;
+}
+
+// ---- key-major plan (dK, dV) ----
+struct KvPlan {
+  std::vector<KvSeg> segs;
+  std::vector<QRef> q;
+  std::vector<Tile> tiles;
+  bool full = false;
+};
+
+dfa_status plan_kv(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n, int tilek,
+                   KvPlan &out) {
+  std::map<PieceKey, std::vector<int64_t>> by_piece;
+  std::vector<PieceKey> order;
+  for (int64_t i = 0; i < n; ++i) {
+    const dfa_block &b = blocks[i];
+    PieceKey key{b.kv_start, b.len_kv, b.stride};
+    auto it = by_piece.find(key);
+    if (it == by_piece.end()) {
+      order.push_back(key);
+      by_piece[key] = {i};
+    } else {
+      it->second.push_back(i);
+    }
+  }
+  if (!pieces_disjoint(order, d->seqlen, out.full)) return DFA_E_SHAPE;
+  struct Cost {
+    int64_t cost;
+    Tile t;
+  };
+  std::vector<Cost> costs;
+  for (const auto &key : order) {
+    auto idx = by_piece[key];
+    std::stable_sort(idx.begin(), idx.end(), [&](int64_t a, int64_t b) {
+      return std::make_tuple(blocks[a].step, blocks[a].q_start) <
+             std::make_tuple(blocks[b].step, blocks[b].q_start);
+    });
+    KvSeg s{};
+    s.kv_start = std::get<0>(key);
+    s.len_kv = std::get<1>(key);
+    s.stride = std::get<2>(key);
+    s.blk_begin = static_cast<int32_t>(out.q.size());
+    s.blk_count = static_cast<int32_t>(idx.size());
+    for (int64_t bi : idx) {
+      if (blocks[bi].stride != s.stride) return DFA_E_SHAPE;
+      out.q.push_back(QRef{blocks[bi].q_start, blocks[bi].len_q, blocks[bi].diag_offset});
+    }
+    const int32_t seg_id = static_cast<int32_t>(out.segs.size());
+    out.segs.push_back(s);
+    const int64_t nt = ceil_div(s.len_kv, tilek);
+    for (int64_t t = 0; t < nt; ++t) {
+      const int64_t j0 = t * tilek;
+      int64_t c = 0;
+      for (int64_t bi : idx) {
+        // query rows i >= j0 - diag see at least one key of the tile
+        const int64_t lo = std::max<int64_t>(0, j0 - blocks[bi].diag_offset);
+        if (lo < blocks[bi].len_q) c += ceil_div(blocks[bi].len_q - lo, kCostTileKV);
+      }
+      costs.push_back(Cost{c, Tile{seg_id, static_cast<int32_t>(t)}});
+    }
+  }
+  std::stable_sort(costs.begin(), costs.end(),
+                   [](const Cost &a, const Cost &b) { return a.cost > b.cost; });
+  out.tiles.reserve(costs.size());
+  for (const auto &c : costs) out.tiles.push_back(c.t);
+  return DFA_OK;
+}
+
+// ---- device table packing ----
+struct Packer {
+  std::vector<char> bytes;
+  template <class T>
+  size_t add(const std::vector<T> &v) {
+    const size_t off = bytes.size();
+    const size_t sz = align_up(v.size() * sizeof(T));
+    bytes.resize(off + std::max<size_t>(sz, kAlign), 0);
+    if (!v.empty()) std::memcpy(bytes.data() + off, v.data(), v.size() * sizeof(T));
+    return off;
+  }
+};
+
+dfa::Geom make_geom(const dfa_attn_desc *d) {
+  dfa::Geom g{};
+  for (int i = 0; i < 3; ++i) {
+    g.qs[i] = d->q_strides[i];
+    g.ks[i] = d->k_strides[i];
+    g.vs[i] = d->v_strides[i];
+    g.os[i] = d->o_strides[i];
+  }
+  g.seqlen = d->seqlen;
+  g.batch = d->batch;
+  g.hq = d->heads_q;
+  g.hkv = d->heads_kv;
+  g.group = d->heads_q / d->heads_kv;
+  g.scale = d->softmax_scale;
+  g.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+  return g;
+}
+
+int fwd_tile(const dfa_attn_desc *d) { return d->dtype == DFA_BF16 ? dfa::kFwdTileQ : dfa::kF32TileQ; }
+int kv_tile(const dfa_attn_desc *d) { return d->dtype == DFA_BF16 ? dfa::kBwdTileKV : dfa::kF32TileKV; }
+
+dfa_status hip_status(hipError_t e) { return e == hipSuccess ? DFA_OK : DFA_E_HIP; }
+
+dfa_status check_blocks(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n) {
+  if (n < 0) return DFA_E_SHAPE;
+  if (n > 0 && !blocks) return DFA_E_NULL;
+  if (n > 0x3fffffff) return DFA_E_SHAPE;
+  for (int64_t i = 0; i < n; ++i) {
+    const dfa_status st = check_block(d, blocks[i]);
+    if (st != DFA_OK) return st;
+  }
+  return DFA_OK;
+}
+
+// Stepwise forward: rounds of blocks whose query pieces are distinct, in
+// ring-step order.
+struct StepPlan {
+  std::vector<QSeg> segs;      // one per block, with its partial-buffer offset
+  std::vector<KvRef> kv;       // one per block
+  std::vector<Tile> tiles;     // per round, contiguous
+  std::vector<MergeItem> items;
+  struct Round {
+    int32_t tile_begin, tile_count, item_begin, item_count;
+    int64_t part_rows, max_len;
+  };
+  std::vector<Round> rounds;
+  int64_t max_part_rows = 0;
+};
+
+void plan_steps(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n, int tileq,
+                StepPlan &sp) {
+  std::vector<int64_t> idx(static_cast<size_t>(n));
+  for (int64_t i = 0; i < n; ++i) idx[i] = i;
+  std::stable_sort(idx.begin(), idx.end(), [&](int64_t a, int64_t b) {
+    return std::make_tuple(blocks[a].step, blocks[a].rank, blocks[a].kv_start) <
+           std::make_tuple(blocks[b].step, blocks[b].rank, blocks[b].kv_start);
+  });
+  const int64_t BH = static_cast<int64_t>(d->batch) * d->heads_q;
+  size_t pos = 0;
+  while (pos < idx.size()) {
+    const int64_t step = blocks[idx[pos]].step;
+    size_t end = pos;
+    while (end < idx.size() && blocks[idx[end]].step == step) ++end;
+    std::vector<std::vector<int64_t>> rounds;
+    std::vector<std::vector<PieceKey>> used;
+    for (size_t p = pos; p < end; ++p) {
+      const dfa_block &b = blocks[idx[p]];
+      PieceKey key{b.q_start, b.len_q, b.stride};
+      size_t r = 0;
+      while (r < rounds.size() &&
+             std::find(used[r].begin(), used[r].end(), key) != used[r].end())
+        ++r;
+      if (r == rounds.size()) {
+        rounds.emplace_back();
+        used.emplace_back();
+      }
+      rounds[r].push_back(idx[p]);
+      used[r].push_back(key);
+    }
+    for (const auto &rb : rounds) {
+      StepPlan::Round R{static_cast<int32_t>(sp.tiles.size()), 0,
+                        static_cast<int32_t>(sp.items.size()), 0, 0, 0};
+      for (int64_t bi : rb) {
+        const dfa_block &b = blocks[bi];
+        QSeg s{};
+        s.q_start = b.q_start;
+        s.len_q = b.len_q;
+        s.stride = b.stride;
+        s.part_off = R.part_rows;
+        s.blk_begin = static_cast<int32_t>(sp.kv.size());
+        s.blk_count = 1;
+        sp.kv.push_back(KvRef{b.kv_start, b.len_kv, b.diag_offset});
+        const int32_t sid = static_cast<int32_t>(sp.segs.size());
+        sp.segs.push_back(s);
+        const int64_t nt = ceil_div(b.len_q, tileq);
+        for (int64_t t = 0; t < nt; ++t) sp.tiles.push_back(Tile{sid, static_cast<int32_t>(t)});
+        sp.items.push_back(MergeItem{b.q_start, b.len_q, b.stride, R.part_rows});
+        R.part_rows += BH * b.len_q;
+        R.max_len = std::max<int64_t>(R.max_len, b.len_q);
+      }
+      R.tile_count = static_cast<int32_t>(sp.tiles.size()) - R.tile_begin;
+      R.item_count = static_cast<int32_t>(sp.items.size()) - R.item_begin;
+      sp.max_part_rows = std::max<int64_t>(sp.max_part_rows, R.part_rows);
+      sp.rounds.push_back(R);
+    }
+    pos = end;
+  }
+}
+
+// Workspace layouts (offsets in bytes).
+struct FusedLayout {
+  size_t segs, kv, tiles, total;
+};
+struct StepLayout {
+  size_t segs, kv, tiles, items, acc_o, acc_lse, part_o, part_lse, total;
+};
+struct BwdLayout {
+  size_t qsegs, qkv, qtiles, kvsegs, kvq, kvtiles, dd, total;
+};
+
+template <class T>
+size_t vbytes(const std::vector<T> &v) {
+  return std::max<size_t>(align_up(v.size() * sizeof(T)), kAlign);
+}
+
+FusedLayout fused_layout(const QPlan &p) {
+  FusedLayout L{};
+  L.segs = 0;
+  L.kv = L.segs + vbytes(p.segs);
+  L.tiles = L.kv + vbytes(p.kv);
+  L.total = L.tiles + vbytes(p.tiles);
+  return L;
+}
+
+StepLayout step_layout(const dfa_attn_desc *d, const StepPlan &p) {
+  StepLayout L{};
+  const size_t hd = static_cast<size_t>(d->head_dim);
+  const size_t rows = static_cast<size_t>(d->batch) * d->heads_q * d->seqlen;
+  L.segs = 0;
+  L.kv = L.segs + vbytes(p.segs);
+  L.tiles = L.kv + vbytes(p.kv);
+  L.items = L.tiles + vbytes(p.tiles);
+  L.acc_o = L.items + vbytes(p.items);
+  L.acc_lse = L.acc_o + align_up(rows * hd * sizeof(float));
+  L.part_o = L.acc_lse + align_up(rows * sizeof(float));
+  L.part_lse = L.part_o + align_up(static_cast<size_t>(p.max_part_rows) * hd * sizeof(float));
+  L.total = L.part_lse + align_up(static_cast<size_t>(p.max_part_rows) * sizeof(float));
+  return L;
+}
+
+BwdLayout bwd_layout(const dfa_attn_desc *d, const QPlan &qp, const KvPlan &kp) {
+  BwdLayout L{};
+  const size_t rows = static_cast<size_t>(d->batch) * d->heads_q * d->seqlen;
+  L.qsegs = 0;
+  L.qkv = L.qsegs + vbytes(qp.segs);
+  L.qtiles = L.qkv + vbytes(qp.kv);
+  L.kvsegs = L.qtiles + vbytes(qp.tiles);
+  L.kvq = L.kvsegs + vbytes(kp.segs);
+  L.kvtiles = L.kvq + vbytes(kp.q);
+  L.dd = L.kvtiles + vbytes(kp.tiles);
+  L.total = L.dd + align_up(rows * sizeof(float));
+  return L;
+}
+
+template <class T>
+void put(std::vector<char> &buf, size_t off, const std::vector<T> &v) {
+  if (!v.empty()) std::memcpy(buf.data() + off, v.data(), v.size() * sizeof(T));
+}
+
+dfa_status upload(void *ws, const std::vector<char> &host, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return DFA_OK;
+  return hip_status(hipMemcpyAsync(ws, host.data(), bytes, hipMemcpyHostToDevice, s));
+}
+
+dfa_status check_ws(void *ws, size_t have, size_t need) {
+  if (need == 0) return DFA_OK;
+  if (!ws) return DFA_E_WORKSPACE;
+  if (have < need) return DFA_E_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return DFA_E_ALIGN;
+  return DFA_OK;
+}
+
+}  // namespace
+
+extern "C" const char *dfa_status_string(dfa_status s) {
+  switch (s) {
+    case DFA_OK: return "ok";
+    case DFA_E_NULL: return "a required pointer is NULL";
+    case DFA_E_SHAPE: return "inconsistent sizes or block list";
+    case DFA_E_UNSUPPORTED: return "unsupported head_dim, dtype, mode or schedule kind";
+    case DFA_E_ALIGN: return "pointer or stride violates 16-byte row alignment";
+    case DFA_E_CAPACITY: return "output array too small";
+    case DFA_E_WORKSPACE: return "workspace missing or too small";
+    case DFA_E_HIP: return "HIP runtime error or kernel launch failure";
+    default: return "unknown status";
+  }
+}
+
+extern "C" dfa_status dfa_workspace_size(const dfa_attn_desc *d, const dfa_block *blocks,
+                                         int64_t n_blocks, int32_t op, size_t *bytes) {
+  if (!bytes) return DFA_E_NULL;
+  dfa_status st = check_desc(d);
+  if (st != DFA_OK) return st;
+  st = check_blocks(d, blocks, n_blocks);
+  if (st != DFA_OK) return st;
+  if (op == DFA_OP_FWD_FUSED) {
+    QPlan p;
+    st = plan_q(d, blocks, n_blocks, fwd_tile(d), p);
+    if (st != DFA_OK) return st;
+    *bytes = fused_layout(p).total;
+  } else if (op == DFA_OP_FWD_STEPWISE) {
+    QPlan p;  // validates piece disjointness
+    st = plan_q(d, blocks, n_blocks, fwd_tile(d), p);
+    if (st != DFA_OK) return st;
+    StepPlan sp;
+    plan_steps(d, blocks, n_blocks, fwd_tile(d), sp);
+    *bytes = step_layout(d, sp).total;
+  } else if (op == DFA_OP_BWD) {
+    QPlan qp;
+    KvPlan kp;
+    st = plan_q(d, blocks, n_blocks, fwd_tile(d), qp);
+    if (st != DFA_OK) return st;
+    st = plan_kv(d, blocks, n_blocks, kv_tile(d), kp);
+    if (st != DFA_OK) return st;
+    *bytes = bwd_layout(d, qp, kp).total;
+  } else {
+    return DFA_E_UNSUPPORTED;
+  }
+  return DFA_OK;
+}
+
+extern "C" dfa_status dfa_attn_block_fwd(const dfa_attn_desc *d, const dfa_block *blk,
+                                         const void *q, const void *k, const void *v,
+                                         float *o_part, float *lse_part, void *stream) {
+  dfa_status st = check_desc(d);
+  if (st != DFA_OK) return st;
+  if (!blk || !q || !k || !v || !o_part || !lse_part) return DFA_E_NULL;
+  st = check_block(d, *blk);
+  if (st != DFA_OK) return st;
+  if (!ptr_aligned(q) || !ptr_aligned(k) || !ptr_aligned(v) || !ptr_aligned(o_part))
+    return DFA_E_ALIGN;
+  dfa::FwdArgs a{};
+  a.g = make_geom(d);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o_part;
+  a.lse = lse_part;
+  a.out_mode = 1;
+  a.seg0 = QSeg{blk->q_start, blk->len_q, blk->stride, 0, 0, 1};
+  a.kv0 = KvRef{blk->kv_start, blk->len_kv, blk->diag_offset};
+  const int tq = fwd_tile(d);
+  const int64_t grid = ceil_div(blk->len_q, tq) * d->batch * d->heads_q;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d->dtype == DFA_BF16) return hip_status(dfa::launch_fwd_bf16(a, d->head_dim, grid, s));
+  return hip_status(dfa::launch_fwd_f32(a, d->head_dim, grid, s));
+}
+
+extern "C" dfa_status dfa_lse_merge(int64_t n_rows, int32_t head_dim, float *o_acc,
+                                    float *lse_acc, const float *o_part, const float *lse_part,
+                                    void *stream) {
+  if (head_dim != 64 && head_dim != 128) return DFA_E_UNSUPPORTED;
+  if (n_rows < 0) return DFA_E_SHAPE;
+  if (n_rows == 0) return DFA_OK;
+  if (!o_acc || !lse_acc || !o_part || !lse_part) return DFA_E_NULL;
+  if (!ptr_aligned(o_acc) || !ptr_aligned(o_part)) return DFA_E_ALIGN;
+  return hip_status(dfa::launch_merge_rows(o_acc, lse_acc, o_part, lse_part, n_rows, head_dim,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+extern "C" dfa_status dfa_attn_fwd(const dfa_attn_desc *d, const dfa_block *blocks,
+                                   int64_t n_blocks, int32_t mode, const void *q, const void *k,
+                                   const void *v, void *o, float *lse, void *workspace,
+                                   size_t ws_bytes, void *stream) {
+  dfa_status st = check_desc(d);
+  if (st != DFA_OK) return st;
+  if (!q || !k || !v || !o || !lse) return DFA_E_NULL;
+  if (!ptr_aligned(q) || !ptr_aligned(k) || !ptr_aligned(v) || !ptr_aligned(o)) return DFA_E_ALIGN;
+  if (mode != DFA_FWD_FUSED && mode != DFA_FWD_STEPWISE) return DFA_E_UNSUPPORTED;
+  st = check_blocks(d, blocks, n_blocks);
+  if (st != DFA_OK) return st;
+  QPlan qp;
+  st = plan_q(d, blocks, n_blocks, fwd_tile(d), qp);
+  if (st != DFA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int hd = d->head_dim;
+  dfa::FwdArgs a{};
+  a.g = make_geom(d);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  auto launch = [&](const dfa::FwdArgs &args, int64_t grid) {
+    return d->dtype == DFA_BF16 ? dfa::launch_fwd_bf16(args, hd, grid, s)
+                                : dfa::launch_fwd_f32(args, hd, grid, s);
+  };
+  const int64_t BH = static_cast<int64_t>(d->batch) * d->heads_q;
+
+  if (mode == DFA_FWD_FUSED) {
+    const FusedLayout L = fused_layout(qp);
+    st = check_ws(workspace, ws_bytes, L.total);
+    if (st != DFA_OK) return st;
+    if (!qp.full) {
+      st = hip_status(dfa::launch_zero_rows(o, d->o_strides, d->dtype, d->batch, d->seqlen,
+                                            d->heads_q, hd, lse, s));
+      if (st != DFA_OK) return st;
+    }
+    if (qp.tiles.empty()) return DFA_OK;
+    std::vector<char> host(L.total, 0);
+    put(host, L.segs, qp.segs);
+    put(host, L.kv, qp.kv);
+    put(host, L.tiles, qp.tiles);
+    st = upload(workspace, host, L.tiles + qp.tiles.size() * sizeof(Tile), s);
+    if (st != DFA_OK) return st;
+    char *ws = static_cast<char *>(workspace);
+    a.o = o;
+    a.lse = lse;
+    a.out_mode = 0;
+    a.segs = reinterpret_cast<const QSeg *>(ws + L.segs);
+    a.kv = reinterpret_cast<const KvRef *>(ws + L.kv);
+    a.tiles = reinterpret_cast<const Tile *>(ws + L.tiles);
+    a.n_tiles = static_cast<int32_t>(qp.tiles.size());
+    return hip_status(launch(a, static_cast<int64_t>(qp.tiles.size()) * BH));
+  }
+
+  // stepwise
+  StepPlan sp;
+  plan_steps(d, blocks, n_blocks, fwd_tile(d), sp);
+  const StepLayout L = step_layout(d, sp);
+  st = check_ws(workspace, ws_bytes, L.total);
+  if (st != DFA_OK) return st;
+  char *ws = static_cast<char *>(workspace);
+  std::vector<char> host(L.acc_o, 0);
+  put(host, L.segs, sp.segs);
+  put(host, L.kv, sp.kv);
+  put(host, L.tiles, sp.tiles);
+  put(host, L.items, sp.items);
+  st = upload(workspace, host, L.acc_o, s);
+  if (st != DFA_OK) return st;
+  float *acc_o = reinterpret_cast<float *>(ws + L.acc_o);
+  float *acc_lse = reinterpret_cast<float *>(ws + L.acc_lse);
+  float *part_o = reinterpret_cast<float *>(ws + L.part_o);
+  float *part_lse = reinterpret_cast<float *>(ws + L.part_lse);
+  const int64_t rows = BH * d->seqlen;
+  st = hip_status(dfa::launch_acc_init(acc_o, acc_lse, rows, hd, s));
+  if (st != DFA_OK) return st;
+  a.o = part_o;
+  a.lse = part_lse;
+  a.out_mode = 1;
+  a.segs = reinterpret_cast<const QSeg *>(ws + L.segs);
+  a.kv = reinterpret_cast<const KvRef *>(ws + L.kv);
+  const MergeItem *items = reinterpret_cast<const MergeItem *>(ws + L.items);
+  for (const auto &R : sp.rounds) {
+    a.tiles = reinterpret_cast<const Tile *>(ws + L.tiles) + R.tile_begin;
+    a.n_tiles = R.tile_count;
+    st = hip_status(launch(a, static_cast<int64_t>(R.tile_count) * BH));
+    if (st != DFA_OK) return st;
+    st = hip_status(dfa::launch_merge_items(acc_o, acc_lse, part_o, part_lse, items + R.item_begin,
+                                            R.item_count, R.max_len, d->batch, d->heads_q,
+                                            d->seqlen, hd, s));
+    if (st != DFA_OK) return st;
+  }
+  return hip_status(dfa::launch_finalize(acc_o, acc_lse, o, d->o_strides, d->dtype, lse,
+                                         d->batch, d->heads_q, d->seqlen, hd, s));
+}
+
+extern "C" dfa_status dfa_attn_bwd(const dfa_attn_desc *d, const dfa_block *blocks,
+                                   int64_t n_blocks, const void *q, const void *k, const void *v,
+                                   const void *o, const void *d_o, const float *lse, void *dq,
+                                   void *dk, void *dv, void *workspace, size_t ws_bytes,
+                                   void *stream) {
+  dfa_status st = check_desc(d);
+  if (st != DFA_OK) return st;
+  if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return DFA_E_NULL;
+  for (const void *p : {q, k, v, o, d_o, static_cast<const void *>(dq),
+                        static_cast<const void *>(dk), static_cast<const void *>(dv)})
+    if (!ptr_aligned(p)) return DFA_E_ALIGN;
+  st = check_blocks(d, blocks, n_blocks);
+  if (st != DFA_OK) return st;
+  QPlan qp;
+  KvPlan kp;
+  st = plan_q(d, blocks, n_blocks, fwd_tile(d), qp);
+  if (st != DFA_OK) return st;
+  st = plan_kv(d, blocks, n_blocks, kv_tile(d), kp);
+  if (st != DFA_OK) return st;
+  const BwdLayout L = bwd_layout(d, qp, kp);
+  st = check_ws(workspace, ws_bytes, L.total);
+  if (st != DFA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int hd = d->head_dim;
+  if (!qp.full) {
+    st = hip_status(dfa::launch_zero_rows(dq, d->q_strides, d->dtype, d->batch, d->seqlen,
+                                          d->heads_q, hd, nullptr, s));
+    if (st != DFA_OK) return st;
+  }
+  if (!kp.full) {
+    st = hip_status(dfa::launch_zero_rows(dk, d->k_strides, d->dtype, d->batch, d->seqlen,
+                                          d->heads_kv, hd, nullptr, s));
+    if (st != DFA_OK) return st;
+    st = hip_status(dfa::launch_zero_rows(dv, d->v_strides, d->dtype, d->batch, d->seqlen,
+                                          d->heads_kv, hd, nullptr, s));
+    if (st != DFA_OK) return st;
+  }
+  if (n_blocks == 0) return DFA_OK;
+  std::vector<char> host(L.dd, 0);
+  put(host, L.qsegs, qp.segs);
+  put(host, L.qkv, qp.kv);
+  put(host, L.qtiles, qp.tiles);
+  put(host, L.kvsegs, kp.segs);
+  put(host, L.kvq, kp.q);
+  put(host, L.kvtiles, kp.tiles);
+  st = upload(workspace, host, L.dd, s);
+  if (st != DFA_OK) return st;
+  char *ws = static_cast<char *>(workspace);
+  dfa::BwdArgs a{};
+  a.g = make_geom(d);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = d_o;
+  a.lse = lse;
+  a.dd = reinterpret_cast<float *>(ws + L.dd);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.qsegs = reinterpret_cast<const QSeg *>(ws + L.qsegs);
+  a.qkv = reinterpret_cast<const KvRef *>(ws + L.qkv);
+  a.qtiles = reinterpret_cast<const Tile *>(ws + L.qtiles);
+  a.n_qtiles = static_cast<int32_t>(qp.tiles.size());
+  a.kvsegs = reinterpret_cast<const KvSeg *>(ws + L.kvsegs);
+  a.kvq = reinterpret_cast<const QRef *>(ws + L.kvq);
+  a.kvtiles = reinterpret_cast<const Tile *>(ws + L.kvtiles);
+  a.n_kvtiles = static_cast<int32_t>(kp.tiles.size());
+  st = hip_status(dfa::launch_bwd_pre(a, d->dtype, hd, s));
+  if (st != DFA_OK) return st;
+  const int64_t BHq = static_cast<int64_t>(d->batch) * d->heads_q;
+  const int64_t BHkv = static_cast<int64_t>(d->batch) * d->heads_kv;
+  if (d->dtype == DFA_BF16) {
+    st = hip_status(dfa::launch_bwd_dq_bf16(a, hd, a.n_qtiles * BHq, s));
+    if (st != DFA_OK) return st;
+    return hip_status(dfa::launch_bwd_dkdv_bf16(a, hd, a.n_kvtiles * BHkv, s));
+  }
+  st = hip_status(dfa::launch_bwd_dq_f32(a, hd, a.n_qtiles * BHq, s));
+  if (st != DFA_OK) return st;
+  return hip_status(dfa::launch_bwd_dkdv_f32(a, hd, a.n_kvtiles * BHkv, s));
+}

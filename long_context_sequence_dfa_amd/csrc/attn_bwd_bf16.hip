@@ -1,0 +1,472 @@
+// attn_bwd_bf16.hip -- bf16 backward of blockwise causal attention on gfx950.
+//
+// The backward keeps no attention matrix: P is recomputed from the saved
+// log-sum-exp (FlashAttention glossary page, first two paragraphs;
+// "rematerialisation-aware gradient checkpointing" on the DistFlashAttn
+// paper record).  With D_i = rowsum(dO_i * O_i):
+//   P_ij = e^{scale q_i.k_j - LSE_i},  dP_ij = dO_i.v_j,  dS_ij = P_ij (dP_ij - D_i)
+//   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i.
+//
+// Two kernels, no atomics, deterministic:
+//  * dq: query-major, shaped like the forward -- a workgroup owns 128 query
+//    rows, walks its query piece's blocks in ring-step order and computes
+//    S^T = K Q^T, dP^T = V dO^T and dQ^T += K^T dS^T on the matrix cores.
+//    Each lane owns one query column, so LSE_i and D_i are per-lane scalars.
+//  * dkdv: key-major -- a workgroup owns 128 key rows (K and V live in
+//    registers as MFMA operands), walks every block that reads its key piece
+//    and every query head of its group, and computes S = Q K^T, dP = dO V^T,
+//    dV^T += dO^T P and dK^T += Q^T dS.  Each lane owns one key column.
+// Q/dO (or K/V) tiles are double-buffered in LDS; transposed operands come
+// from ds_read_b64_tr_b16 on the row-major tiles.
+#include "device_util.h"
+#include "dfa_internal.h"
+
+namespace dfa {
+namespace {
+
+constexpr int NT = 256;
+
+__device__ __forceinline__ int kperm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// ============================ dQ (query-major) ============================
+constexpr int DQ_BQ = kFwdTileQ;  // 128
+constexpr int DQ_BK = 64;
+
+template <int HD>
+__global__ __launch_bounds__(NT, 2) void dq_bf16_kernel(BwdArgs a) {
+  constexpr int PITCH = HD * 2 + 32;
+  constexpr int TILEB = DQ_BK * PITCH;
+  constexpr int KS = HD / 16, DT = HD / 32, CH = HD / 8, RPP = NT / CH, NP = DQ_BK / RPP;
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILEB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, c32 = lane & 31;
+  const Geom &G = a.g;
+  const int BH = G.batch * G.hq;
+  const int64_t bid = blockIdx.x;
+  const int bh = static_cast<int>(bid % BH);
+  const Tile tl = a.qtiles[bid / BH];
+  const QSeg seg = a.qsegs[tl.seg];
+  const int b = bh / G.hq, h = bh % G.hq, hk = h / G.group;
+  const int64_t i0 = static_cast<int64_t>(tl.tile) * DQ_BQ;
+  const int64_t i0w = i0 + wave * 32;
+  const int64_t iend = (i0 + DQ_BQ < seg.len_q) ? i0 + DQ_BQ : seg.len_q;
+
+  const char *kb = static_cast<const char *>(a.k) + 2 * (b * G.ks[0] + hk * G.ks[2]);
+  const char *vb = static_cast<const char *>(a.v) + 2 * (b * G.vs[0] + hk * G.vs[2]);
+
+  bf16x8 qf[KS], df[KS];
+  float lse2 = 0.f, dd = 0.f;
+  const int64_t row = i0w + c32;
+  const bool valid = row < seg.len_q;
+  int64_t pos = 0;
+  if (valid) {
+    pos = seg.q_start + row * seg.stride;
+    const char *qsrc = static_cast<const char *>(a.q) + 2 * (b * G.qs[0] + pos * G.qs[1] + h * G.qs[2]);
+    const char *dsrc = static_cast<const char *>(a.dout) + 2 * (b * G.os[0] + pos * G.os[1] + h * G.os[2]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = __builtin_bit_cast(bf16x8, ld16(qsrc + (2 * ks + g) * 16));
+      df[ks] = __builtin_bit_cast(bf16x8, ld16(dsrc + (2 * ks + g) * 16));
+    }
+    const int64_t r = (static_cast<int64_t>(b) * G.hq + h) * G.seqlen + pos;
+    lse2 = a.lse[r] * kLog2e;
+    dd = a.dd[r];
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = df[ks] = bf16x8{};
+  }
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+
+  struct Walk {
+    int64_t kv_start, len_kv, diag, ntiles;
+  };
+  auto walk = [&](int k) {
+    const KvRef r = a.qkv[seg.blk_begin + k];
+    Walk w{r.kv_start, r.len_kv, r.diag_offset, 0};
+    int64_t hi = iend + r.diag_offset;
+    if (hi > r.len_kv) hi = r.len_kv;
+    w.ntiles = hi > 0 ? (hi + DQ_BK - 1) / DQ_BK : 0;
+    return w;
+  };
+  const int nblk = seg.blk_count;
+  int k = 0;
+  Walk cw{0, 0, 0, 0};
+  while (k < nblk) {
+    cw = walk(k);
+    if (cw.ntiles > 0) break;
+    ++k;
+  }
+  const int lrow = tid / CH, lch = tid % CH;
+  u32x4 kr[NP], vr[NP];
+  auto gload = [&](const Walk &w, int64_t t) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int64_t j = t * DQ_BK + lrow + p * RPP;
+      if (j < w.len_kv) {
+        const int64_t kp = w.kv_start + j * seg.stride;
+        kr[p] = ld16(kb + 2 * kp * G.ks[1] + lch * 16);
+        vr[p] = ld16(vb + 2 * kp * G.vs[1] + lch * 16);
+      } else {
+        kr[p] = u32x4{0, 0, 0, 0};
+        vr[p] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+    char *kt = smem + buf * 2 * TILEB;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      st16(kt + (lrow + p * RPP) * PITCH + lch * 16, kr[p]);
+      st16(kt + TILEB + (lrow + p * RPP) * PITCH + lch * 16, vr[p]);
+    }
+  };
+  int64_t t = 0;
+  int cur = 0;
+  if (k < nblk) {
+    gload(cw, 0);
+    lstore(0);
+  }
+  __syncthreads();
+  while (k < nblk) {
+    int kn = k;
+    int64_t tn = t + 1;
+    Walk nw = cw;
+    if (tn >= cw.ntiles) {
+      tn = 0;
+      ++kn;
+      while (kn < nblk) {
+        nw = walk(kn);
+        if (nw.ntiles > 0) break;
+        ++kn;
+      }
+    }
+    const bool have_next = kn < nblk;
+    if (have_next) gload(nw, tn);
+
+    const int64_t j0 = t * DQ_BK;
+    if (j0 <= i0w + 31 + cw.diag) {
+      const char *kt = smem + cur * 2 * TILEB;
+      const char *vt = kt + TILEB;
+      f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
+      const int ro = kperm(c32) * PITCH + g * 16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 k0 = __builtin_bit_cast(bf16x8, ld16(kt + ro + ks * 32));
+        const bf16x8 k1 = __builtin_bit_cast(bf16x8, ld16(kt + ro + 32 * PITCH + ks * 32));
+        const bf16x8 v0 = __builtin_bit_cast(bf16x8, ld16(vt + ro + ks * 32));
+        const bf16x8 v1 = __builtin_bit_cast(bf16x8, ld16(vt + ro + 32 * PITCH + ks * 32));
+        s0 = mfma32(k0, qf[ks], s0);
+        s1 = mfma32(k1, qf[ks], s1);
+        p0 = mfma32(v0, df[ks], p0);
+        p1 = mfma32(v1, df[ks], p1);
+      }
+      const bool need_mask = (j0 + DQ_BK - 1 > i0w + cw.diag) || (j0 + DQ_BK > cw.len_kv);
+      const int64_t lim = row + cw.diag;
+      bf16x8 dsb[4];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float s = (i < 16 ? s0[i] : s1[i - 16]);
+        const float dp = (i < 16 ? p0[i] : p1[i - 16]);
+        float p = fast_exp2(s * G.scale_log2 - lse2);
+        if (need_mask) {
+          const int64_t j = j0 + 32 * (i / 16) + 16 * ((i % 16) / 8) + 8 * g + (i % 8);
+          if (j > lim || j >= cw.len_kv) p = 0.f;
+        }
+        dsb[i / 8][i % 8] = static_cast<__bf16>(p * (dp - dd));
+      }
+      // dQ^T += K^T dS^T: A = K^T (d x 16 keys) read transposed from the K tile
+      const int krow = 8 * g + (lane & 15) / 4;
+      const int kcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const char *kp = kt + (16 * kk + krow) * PITCH + kcol * 2;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x4 lo = lds_read_tr(kp + dt * 64);
+          const bf16x4 hi = lds_read_tr(kp + 4 * PITCH + dt * 64);
+          acc[dt] = mfma32(cat8(lo, hi), dsb[kk], acc[dt]);
+        }
+      }
+    }
+    if (have_next) lstore(cur ^ 1);
+    __syncthreads();
+    cur ^= 1;
+    k = kn;
+    t = tn;
+    cw = nw;
+  }
+  if (!valid) return;
+  char *ob = static_cast<char *>(a.dq) + 2 * (b * G.qs[0] + pos * G.qs[1] + h * G.qs[2]);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = static_cast<__bf16>(acc[dt][4 * q4 + e] * G.scale);
+      *reinterpret_cast<bf16x4 *>(ob + 2 * (32 * dt + 8 * q4 + 4 * g)) = v;
+    }
+}
+
+// ========================= dK, dV (key-major) =========================
+constexpr int KV_BK = kBwdTileKV;  // 128 key rows per workgroup
+constexpr int KV_BQ = 64;          // query rows per streamed tile
+
+template <int HD>
+__global__ __launch_bounds__(NT, 1) void dkdv_bf16_kernel(BwdArgs a) {
+  constexpr int PITCH = HD * 2 + 32;
+  constexpr int TILEB = KV_BQ * PITCH;
+  constexpr int BUFB = 2 * TILEB + 2 * KV_BQ * 4;  // Q, dO, lse*log2e, D
+  constexpr int KS = HD / 16, DT = HD / 32, CH = HD / 8, RPP = NT / CH, NP = KV_BQ / RPP;
+  __shared__ __attribute__((aligned(16))) char smem[2 * BUFB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, c32 = lane & 31;
+  const Geom &G = a.g;
+  const int BH = G.batch * G.hkv;
+  const int64_t bid = blockIdx.x;
+  const int bh = static_cast<int>(bid % BH);
+  const Tile tl = a.kvtiles[bid / BH];
+  const KvSeg seg = a.kvsegs[tl.seg];
+  const int b = bh / G.hkv, hk = bh % G.hkv;
+  const int64_t j0 = static_cast<int64_t>(tl.tile) * KV_BK;
+  const int64_t j0w = j0 + wave * 32;
+  const int64_t col = j0w + c32;  // this lane's key row
+  const bool valid = col < seg.len_kv;
+
+  // K and V as B operands of S = Q K^T and dP = dO V^T
+  bf16x8 kf[KS], vf[KS];
+  int64_t pos = 0;
+  if (valid) {
+    pos = seg.kv_start + col * seg.stride;
+    const char *ksrc = static_cast<const char *>(a.k) + 2 * (b * G.ks[0] + pos * G.ks[1] + hk * G.ks[2]);
+    const char *vsrc = static_cast<const char *>(a.v) + 2 * (b * G.vs[0] + pos * G.vs[1] + hk * G.vs[2]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = __builtin_bit_cast(bf16x8, ld16(ksrc + (2 * ks + g) * 16));
+      vf[ks] = __builtin_bit_cast(bf16x8, ld16(vsrc + (2 * ks + g) * 16));
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = vf[ks] = bf16x8{};
+  }
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dk[dt] = dv[dt] = f32x16{};
+
+  // walk over (group head, block, query tile)
+  struct Walk {
+    int64_t q_start, len_q, diag, t0, t1;  // query tiles [t0, t1)
+    int h;
+  };
+  auto walk = [&](int gi, int k) {
+    const QRef r = a.kvq[seg.blk_begin + k];
+    Walk w{r.q_start, r.len_q, r.diag_offset, 0, 0, hk * G.group + gi};
+    int64_t lo = j0 - r.diag_offset;  // first query row that sees key row j0
+    if (lo < 0) lo = 0;
+    if (lo < r.len_q) {
+      w.t0 = lo / KV_BQ;
+      w.t1 = (r.len_q + KV_BQ - 1) / KV_BQ;
+    }
+    return w;
+  };
+  const int nblk = seg.blk_count, ngrp = G.group;
+  int gi = 0, k = 0;
+  Walk cw{};
+  auto advance_to_nonempty = [&](int &gi_, int &k_, Walk &w_) {
+    while (gi_ < ngrp) {
+      while (k_ < nblk) {
+        w_ = walk(gi_, k_);
+        if (w_.t1 > w_.t0) return;
+        ++k_;
+      }
+      ++gi_;
+      k_ = 0;
+    }
+  };
+  advance_to_nonempty(gi, k, cw);
+  int64_t t = cw.t0;
+
+  const int lrow = tid / CH, lch = tid % CH;
+  u32x4 qr[NP], dr[NP];
+  float lsr = 0.f, ddr = 0.f;
+  auto gload = [&](const Walk &w, int64_t tt) {
+    const char *qb = static_cast<const char *>(a.q) + 2 * (b * G.qs[0] + w.h * G.qs[2]);
+    const char *db = static_cast<const char *>(a.dout) + 2 * (b * G.os[0] + w.h * G.os[2]);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int64_t i = tt * KV_BQ + lrow + p * RPP;
+      if (i < w.len_q) {
+        const int64_t qp = w.q_start + i * seg.stride;
+        qr[p] = ld16(qb + 2 * qp * G.qs[1] + lch * 16);
+        dr[p] = ld16(db + 2 * qp * G.os[1] + lch * 16);
+      } else {
+        qr[p] = u32x4{0, 0, 0, 0};
+        dr[p] = u32x4{0, 0, 0, 0};
+      }
+    }
+    if (tid < KV_BQ) {
+      const int64_t i = tt * KV_BQ + tid;
+      if (i < w.len_q) {
+        const int64_t r = (static_cast<int64_t>(b) * G.hq + w.h) * G.seqlen + w.q_start + i * seg.stride;
+        lsr = a.lse[r] * kLog2e;
+        ddr = a.dd[r];
+      } else {
+        lsr = INFINITY;  // rows past the piece contribute P = 0
+        ddr = 0.f;
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+    char *base = smem + buf * BUFB;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      st16(base + (lrow + p * RPP) * PITCH + lch * 16, qr[p]);
+      st16(base + TILEB + (lrow + p * RPP) * PITCH + lch * 16, dr[p]);
+    }
+    if (tid < KV_BQ) {
+      reinterpret_cast<float *>(base + 2 * TILEB)[tid] = lsr;
+      reinterpret_cast<float *>(base + 2 * TILEB + KV_BQ * 4)[tid] = ddr;
+    }
+  };
+
+  int cur = 0;
+  if (gi < ngrp) {
+    gload(cw, t);
+    lstore(0);
+  }
+  __syncthreads();
+  while (gi < ngrp) {
+    int gn = gi, kn = k;
+    int64_t tn = t + 1;
+    Walk nw = cw;
+    if (tn >= cw.t1) {
+      ++kn;
+      advance_to_nonempty(gn, kn, nw);
+      tn = nw.t0;
+    }
+    const bool have_next = gn < ngrp;
+    if (have_next) gload(nw, tn);
+
+    const int64_t qi0 = t * KV_BQ;
+    // some pair of this wave visible: largest query row sees smallest key row
+    if (qi0 + KV_BQ - 1 + cw.diag >= j0w) {
+      const char *qt = smem + cur * BUFB;
+      const char *dt_ = qt + TILEB;
+      const float *lt = reinterpret_cast<const float *>(qt + 2 * TILEB);
+      const float *ddt = lt + KV_BQ;
+      f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
+      const int ro = kperm(c32) * PITCH + g * 16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 q0 = __builtin_bit_cast(bf16x8, ld16(qt + ro + ks * 32));
+        const bf16x8 q1 = __builtin_bit_cast(bf16x8, ld16(qt + ro + 32 * PITCH + ks * 32));
+        const bf16x8 d0 = __builtin_bit_cast(bf16x8, ld16(dt_ + ro + ks * 32));
+        const bf16x8 d1 = __builtin_bit_cast(bf16x8, ld16(dt_ + ro + 32 * PITCH + ks * 32));
+        s0 = mfma32(q0, kf[ks], s0);
+        s1 = mfma32(q1, kf[ks], s1);
+        p0 = mfma32(d0, vf[ks], p0);
+        p1 = mfma32(d1, vf[ks], p1);
+      }
+      // element i of s0/s1 is query row qi0 + 32*(i/16) + 16*((i%16)/8) + 8g + i%8
+      const bool need_mask = (qi0 + cw.diag < j0w + 31) || (qi0 + KV_BQ > cw.len_q);
+      bf16x8 pb[4], dsb[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int qoff = 16 * kk + 8 * g;
+        const f32x4 la = *reinterpret_cast<const f32x4 *>(lt + qoff);
+        const f32x4 lb = *reinterpret_cast<const f32x4 *>(lt + qoff + 4);
+        const f32x4 da = *reinterpret_cast<const f32x4 *>(ddt + qoff);
+        const f32x4 db = *reinterpret_cast<const f32x4 *>(ddt + qoff + 4);
+#pragma unroll
+        for (int w = 0; w < 8; ++w) {
+          const int i = 8 * kk + w;
+          const float s = (i < 16 ? s0[i] : s1[i - 16]);
+          const float dp = (i < 16 ? p0[i] : p1[i - 16]);
+          const float l2 = w < 4 ? la[w] : lb[w - 4];
+          const float D = w < 4 ? da[w] : db[w - 4];
+          float p = fast_exp2(s * G.scale_log2 - l2);
+          if (need_mask) {
+            const int64_t qi = qi0 + qoff + w;
+            if (col > qi + cw.diag) p = 0.f;
+          }
+          pb[kk][w] = static_cast<__bf16>(p);
+          dsb[kk][w] = static_cast<__bf16>(p * (dp - D));
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS: A operands read transposed from LDS
+      const int trow = 8 * g + (lane & 15) / 4;
+      const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const char *dp_ = dt_ + (16 * kk + trow) * PITCH + tcol * 2;
+        const char *qp_ = qt + (16 * kk + trow) * PITCH + tcol * 2;
+#pragma unroll
+        for (int dd_ = 0; dd_ < DT; ++dd_) {
+          const bf16x4 dlo = lds_read_tr(dp_ + dd_ * 64);
+          const bf16x4 dhi = lds_read_tr(dp_ + 4 * PITCH + dd_ * 64);
+          dv[dd_] = mfma32(cat8(dlo, dhi), pb[kk], dv[dd_]);
+          const bf16x4 qlo = lds_read_tr(qp_ + dd_ * 64);
+          const bf16x4 qhi = lds_read_tr(qp_ + 4 * PITCH + dd_ * 64);
+          dk[dd_] = mfma32(cat8(qlo, qhi), dsb[kk], dk[dd_]);
+        }
+      }
+    }
+    if (have_next) lstore(cur ^ 1);
+    __syncthreads();
+    cur ^= 1;
+    gi = gn;
+    k = kn;
+    t = tn;
+    cw = nw;
+  }
+  if (!valid) return;
+  char *okb = static_cast<char *>(a.dk) + 2 * (b * G.ks[0] + pos * G.ks[1] + hk * G.ks[2]);
+  char *ovb = static_cast<char *>(a.dv) + 2 * (b * G.vs[0] + pos * G.vs[1] + hk * G.vs[2]);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      bf16x4 x, y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = static_cast<__bf16>(dk[dt][4 * q4 + e] * G.scale);
+        y[e] = static_cast<__bf16>(dv[dt][4 * q4 + e]);
+      }
+      const int d0 = 32 * dt + 8 * q4 + 4 * g;
+      *reinterpret_cast<bf16x4 *>(okb + 2 * d0) = x;
+      *reinterpret_cast<bf16x4 *>(ovb + 2 * d0) = y;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dq_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (hd == 128)
+    hipLaunchKernelGGL(dq_bf16_kernel<128>, dim3(static_cast<unsigned>(grid)), dim3(NT), 0, s, a);
+  else if (hd == 64)
+    hipLaunchKernelGGL(dq_bf16_kernel<64>, dim3(static_cast<unsigned>(grid)), dim3(NT), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (hd == 128)
+    hipLaunchKernelGGL(dkdv_bf16_kernel<128>, dim3(static_cast<unsigned>(grid)), dim3(NT), 0, s, a);
+  else if (hd == 64)
+    hipLaunchKernelGGL(dkdv_bf16_kernel<64>, dim3(static_cast<unsigned>(grid)), dim3(NT), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace dfa

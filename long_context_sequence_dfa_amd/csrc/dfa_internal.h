@@ -1,0 +1,123 @@
+// dfa_internal.h -- device-side work tables and kernel launchers shared by the
+// host runtime (api.cpp) and the HIP kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dfa {
+
+// One distinct query piece: local row i sits at global position
+// q_start + i*stride.  Its blocks (key pieces in ring-step order) are
+// kv[blk_begin, blk_begin + blk_count).
+struct QSeg {
+  int64_t q_start, len_q, stride;
+  int64_t part_off;  // stepwise/block mode: float offset of this piece's partial buffer
+  int32_t blk_begin, blk_count;
+};
+
+// One key piece seen by a query piece, with the block's diagonal offset:
+// local key j is visible to local query i iff j <= i + diag_offset.
+struct KvRef {
+  int64_t kv_start, len_kv, diag_offset;
+};
+
+// One distinct key piece (backward, key-major walk) and the query pieces
+// that read it: q[blk_begin, blk_begin + blk_count).
+struct KvSeg {
+  int64_t kv_start, len_kv, stride;
+  int32_t blk_begin, blk_count;
+};
+
+struct QRef {
+  int64_t q_start, len_q, diag_offset;
+};
+
+// A unit of work: tile `tile` of piece `seg`.
+struct Tile {
+  int32_t seg, tile;
+};
+
+// Geometry of one attention problem as the kernels see it.
+struct Geom {
+  int64_t qs[3], ks[3], vs[3], os[3];  // element strides (batch, token, head)
+  int64_t seqlen;
+  int32_t batch, hq, hkv, group;  // group = hq / hkv
+  float scale_log2;               // softmax scale * log2(e)
+  float scale;                    // softmax scale
+};
+
+// Forward over query pieces (fused walk, stepwise rounds, single block).
+struct FwdArgs {
+  Geom g;
+  const void *q, *k, *v;
+  void *o;        // out_mode 0: dtype O (strides g.os); 1: fp32 partial buffer base
+  float *lse;     // out_mode 0: [B][Hq][N]; 1: partial LSE base (float offset part_off/hd)
+  const QSeg *segs;
+  const KvRef *kv;
+  const Tile *tiles;
+  int32_t n_tiles;
+  int32_t out_mode;  // 0: final O/LSE at global rows; 1: fp32 partials per piece
+  QSeg seg0;         // used when segs == nullptr (one block, no table)
+  KvRef kv0;
+};
+
+// Backward arguments.
+struct BwdArgs {
+  Geom g;
+  const void *q, *k, *v, *o, *dout;
+  const float *lse;  // [B][Hq][N]
+  float *dd;         // D = rowsum(dO*O): [B][Hq][N]
+  void *dq, *dk, *dv;
+  const QSeg *qsegs;
+  const KvRef *qkv;    // key pieces per query piece (dq walk)
+  const Tile *qtiles;
+  int32_t n_qtiles;
+  const KvSeg *kvsegs;
+  const QRef *kvq;     // query pieces per key piece (dk/dv walk)
+  const Tile *kvtiles;
+  int32_t n_kvtiles;
+};
+
+// Row map of one partial buffer onto accumulator rows (stepwise merge).
+struct MergeItem {
+  int64_t q_start, len_q, stride, part_off;
+};
+
+// Tile shapes (rows per work item).
+constexpr int kFwdTileQ = 128;   // bf16 forward / dq: query rows per workgroup
+constexpr int kBwdTileKV = 128;  // bf16 dk/dv: key rows per workgroup
+constexpr int kF32TileQ = 64;    // fp32 kernels: rows per workgroup
+constexpr int kF32TileKV = 64;
+
+// ---- launchers (return hipError_t of the launch) ----
+hipError_t launch_fwd_bf16(const FwdArgs &a, int hd, int64_t grid, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs &a, int hd, int64_t grid, hipStream_t s);
+hipError_t launch_bwd_pre(const BwdArgs &a, int dtype, int hd, hipStream_t s);
+hipError_t launch_bwd_dq_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_t s);
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_t s);
+hipError_t launch_bwd_dq_f32(const BwdArgs &a, int hd, int64_t grid, hipStream_t s);
+hipError_t launch_bwd_dkdv_f32(const BwdArgs &a, int hd, int64_t grid, hipStream_t s);
+
+// Fill rows of a [B][N][H][hd] tensor (strides) with zero; if lse != nullptr
+// also set lse [B][H][N] to -inf.
+hipError_t launch_zero_rows(void *x, const int64_t strides[3], int dtype, int batch, int64_t n,
+                            int heads, int hd, float *lse, hipStream_t s);
+// acc <- identity (O = 0, LSE = -inf) for [rows][hd] fp32 + [rows].
+hipError_t launch_acc_init(float *o_acc, float *lse_acc, int64_t rows, int hd, hipStream_t s);
+// Merge partial rows into accumulators.  Item k of `items` maps its partial
+// rows [b][h][i] (at part_off) onto accumulator rows [b][h][q_start + i*stride]
+// of an accumulator [B][Hq][N][hd].
+hipError_t launch_merge_items(float *o_acc, float *lse_acc, const float *o_part,
+                              const float *lse_part, const MergeItem *items, int n_items,
+                              int64_t max_rows, int batch, int hq, int64_t n, int hd,
+                              hipStream_t s);
+// Plain contiguous merge of n_rows rows (public dfa_lse_merge).
+hipError_t launch_merge_rows(float *o_acc, float *lse_acc, const float *o_part,
+                             const float *lse_part, int64_t n_rows, int hd, hipStream_t s);
+// Accumulator [B][Hq][N][hd] fp32 -> O (dtype, strides) and lse [B][Hq][N].
+hipError_t launch_finalize(const float *o_acc, const float *lse_acc, void *o,
+                           const int64_t os[3], int dtype, float *lse, int batch, int hq,
+                           int64_t n, int hd, hipStream_t s);
+
+}  // namespace dfa

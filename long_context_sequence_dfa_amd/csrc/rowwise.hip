@@ -1,0 +1,260 @@
+// rowwise.hip -- HBM-bound row kernels: accumulator init, log-sum-exp merge,
+// finalisation, zero fill and the backward's D = rowsum(dO * O).
+//
+// Merge rule (Striped Attention Guide, "Algorithmic Mechanics" 1, steps 4-7,
+// written for partials that are already normalised): with
+// M = max(LSE_a, LSE_b), LSE = M + ln(e^{LSE_a-M} + e^{LSE_b-M}) and
+// O = e^{LSE_a-LSE} O_a + e^{LSE_b-LSE} O_b.  Two empty rows (LSE = -inf)
+// merge to O = 0, LSE = -inf: the max is tested before any subtraction, so
+// -inf - -inf never occurs.
+#include "device_util.h"
+#include "dfa_internal.h"
+
+namespace dfa {
+namespace {
+
+constexpr int NT = 256;
+
+__device__ __forceinline__ void merge_weights(float la, float lp, float &wa, float &wp,
+                                              float &lse) {
+  const float M = fmaxf(la, lp);
+  if (M == -INFINITY) {
+    wa = 0.f;
+    wp = 0.f;
+    lse = -INFINITY;
+    return;
+  }
+  const float ea = expf(la - M), ep = expf(lp - M);
+  lse = M + logf(ea + ep);
+  wa = expf(la - lse);
+  wp = expf(lp - lse);
+}
+
+// one thread per (row, 4 floats); HD/4 threads of a row sit in one wave
+template <int HD>
+__global__ __launch_bounds__(NT) void merge_items_kernel(float *o_acc, float *lse_acc,
+                                                         const float *o_part,
+                                                         const float *lse_part,
+                                                         const MergeItem *items, int batch,
+                                                         int hq, int64_t n) {
+  constexpr int C4 = HD / 4;
+  const MergeItem it = items[blockIdx.y];
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
+  const int64_t rows = static_cast<int64_t>(batch) * hq * it.len_q;
+  if (tid >= rows * C4) return;
+  const int64_t prow = tid / C4;
+  const int c = static_cast<int>(tid % C4);
+  const int64_t bh = prow / it.len_q, i = prow % it.len_q;
+  const int64_t arow = bh * n + it.q_start + i * it.stride;
+  const float lp = lse_part[it.part_off + prow];
+  const float la = lse_acc[arow];
+  float wa, wp, lse;
+  merge_weights(la, lp, wa, wp, lse);
+  f32x4 *oa = reinterpret_cast<f32x4 *>(o_acc + arow * HD) + c;
+  const f32x4 op = reinterpret_cast<const f32x4 *>(o_part + (it.part_off + prow) * HD)[c];
+  const f32x4 av = *oa;
+  f32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = (wa == 0.f ? 0.f : wa * av[e]) + (wp == 0.f ? 0.f : wp * op[e]);
+  *oa = r;
+  if (c == 0) lse_acc[arow] = lse;
+}
+
+template <int HD>
+__global__ __launch_bounds__(NT) void merge_rows_kernel(float *o_acc, float *lse_acc,
+                                                        const float *o_part,
+                                                        const float *lse_part, int64_t n_rows) {
+  constexpr int C4 = HD / 4;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
+  if (tid >= n_rows * C4) return;
+  const int64_t r = tid / C4;
+  const int c = static_cast<int>(tid % C4);
+  float wa, wp, lse;
+  merge_weights(lse_acc[r], lse_part[r], wa, wp, lse);
+  f32x4 *oa = reinterpret_cast<f32x4 *>(o_acc + r * HD) + c;
+  const f32x4 op = reinterpret_cast<const f32x4 *>(o_part + r * HD)[c];
+  const f32x4 av = *oa;
+  f32x4 res;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    res[e] = (wa == 0.f ? 0.f : wa * av[e]) + (wp == 0.f ? 0.f : wp * op[e]);
+  *oa = res;
+  if (c == 0) lse_acc[r] = lse;
+}
+
+__global__ __launch_bounds__(NT) void acc_init_kernel(float *o_acc, float *lse_acc, int64_t rows,
+                                                      int hd) {
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
+  const int64_t c4 = hd / 4;
+  if (tid < rows * c4) reinterpret_cast<f32x4 *>(o_acc)[tid] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (tid < rows) lse_acc[tid] = -INFINITY;
+}
+
+// acc [B][Hq][N][HD] -> O[b][pos][h][:] (dtype) and lse [B][Hq][N]
+template <int HD, bool BF16>
+__global__ __launch_bounds__(NT) void finalize_kernel(const float *o_acc, const float *lse_acc,
+                                                      void *o, int64_t os0, int64_t os1,
+                                                      int64_t os2, float *lse, int hq,
+                                                      int64_t n, int64_t rows) {
+  constexpr int C4 = HD / 4;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
+  if (tid >= rows * C4) return;
+  const int64_t r = tid / C4;
+  const int c = static_cast<int>(tid % C4);
+  const int64_t bh = r / n, pos = r % n;
+  const int64_t b = bh / hq, h = bh % hq;
+  const f32x4 v = reinterpret_cast<const f32x4 *>(o_acc + r * HD)[c];
+  const int64_t off = b * os0 + pos * os1 + h * os2 + 4 * c;
+  if (BF16) {
+    bf16x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = static_cast<__bf16>(v[e]);
+    *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(o) + off) = w;
+  } else {
+    *reinterpret_cast<f32x4 *>(static_cast<float *>(o) + off) = v;
+  }
+  if (c == 0) lse[r] = lse_acc[r];
+}
+
+// x[b][t][h][:] = 0 for every row (16 bytes per thread); lse = -inf
+__global__ __launch_bounds__(NT) void zero_rows_kernel(char *x, int64_t s0, int64_t s1, int64_t s2,
+                                                       int esize, int heads, int64_t n,
+                                                       int row_bytes, float *lse, int64_t rows) {
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
+  const int c16 = row_bytes / 16;
+  if (tid < rows * c16) {
+    const int64_t r = tid / c16;
+    const int c = static_cast<int>(tid % c16);
+    const int64_t b = r / (n * heads), rem = r % (n * heads);
+    const int64_t t = rem / heads, h = rem % heads;
+    st16(x + esize * (b * s0 + t * s1 + h * s2) + 16 * c, u32x4{0, 0, 0, 0});
+  }
+  if (lse && tid < rows) lse[tid] = -INFINITY;  // [B][H][N] has the same row count
+}
+
+// D[b][h][pos] = sum_c dO[b][pos][h][c] * O[b][pos][h][c]: one thread per row
+template <int HD, bool BF16>
+__global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdArgs a) {
+  const Geom &G = a.g;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
+  const int64_t rows = static_cast<int64_t>(G.batch) * G.hq * G.seqlen;
+  if (tid >= rows) return;
+  const int64_t bh = tid / G.seqlen, pos = tid % G.seqlen;
+  const int64_t b = bh / G.hq, h = bh % G.hq;
+  const int64_t off = b * G.os[0] + pos * G.os[1] + h * G.os[2];
+  float s = 0.f;
+  if (BF16) {
+    const uint16_t *op = static_cast<const uint16_t *>(a.o) + off;
+    const uint16_t *dp = static_cast<const uint16_t *>(a.dout) + off;
+#pragma unroll
+    for (int c = 0; c < HD; c += 8) {
+      const u32x4 ov = ld16(op + c), dv = ld16(dp + c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s = fmaf(__uint_as_float(ov[e] << 16), __uint_as_float(dv[e] << 16), s);
+        s = fmaf(__uint_as_float(ov[e] & 0xffff0000u), __uint_as_float(dv[e] & 0xffff0000u), s);
+      }
+    }
+  } else {
+    const float *op = static_cast<const float *>(a.o) + off;
+    const float *dp = static_cast<const float *>(a.dout) + off;
+#pragma unroll
+    for (int c = 0; c < HD; c += 4) {
+      const f32x4 ov = *reinterpret_cast<const f32x4 *>(op + c);
+      const f32x4 dv = *reinterpret_cast<const f32x4 *>(dp + c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = fmaf(ov[e], dv[e], s);
+    }
+  }
+  a.dd[tid] = s;
+}
+
+inline unsigned blocks_for(int64_t threads) { return static_cast<unsigned>((threads + NT - 1) / NT); }
+
+}  // namespace
+
+hipError_t launch_acc_init(float *o_acc, float *lse_acc, int64_t rows, int hd, hipStream_t s) {
+  const int64_t th = rows * (hd / 4) > rows ? rows * (hd / 4) : rows;
+  if (th == 0) return hipSuccess;
+  hipLaunchKernelGGL(acc_init_kernel, dim3(blocks_for(th)), dim3(NT), 0, s, o_acc, lse_acc, rows, hd);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_items(float *o_acc, float *lse_acc, const float *o_part,
+                              const float *lse_part, const MergeItem *items, int n_items,
+                              int64_t max_rows, int batch, int hq, int64_t n, int hd,
+                              hipStream_t s) {
+  if (n_items == 0 || max_rows == 0) return hipSuccess;
+  const int64_t th = static_cast<int64_t>(batch) * hq * max_rows * (hd / 4);
+  dim3 gr(blocks_for(th), n_items);
+  if (hd == 128)
+    hipLaunchKernelGGL(merge_items_kernel<128>, gr, dim3(NT), 0, s, o_acc, lse_acc, o_part,
+                       lse_part, items, batch, hq, n);
+  else
+    hipLaunchKernelGGL(merge_items_kernel<64>, gr, dim3(NT), 0, s, o_acc, lse_acc, o_part,
+                       lse_part, items, batch, hq, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_rows(float *o_acc, float *lse_acc, const float *o_part,
+                             const float *lse_part, int64_t n_rows, int hd, hipStream_t s) {
+  if (n_rows == 0) return hipSuccess;
+  const int64_t th = n_rows * (hd / 4);
+  if (hd == 128)
+    hipLaunchKernelGGL(merge_rows_kernel<128>, dim3(blocks_for(th)), dim3(NT), 0, s, o_acc,
+                       lse_acc, o_part, lse_part, n_rows);
+  else
+    hipLaunchKernelGGL(merge_rows_kernel<64>, dim3(blocks_for(th)), dim3(NT), 0, s, o_acc,
+                       lse_acc, o_part, lse_part, n_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const float *o_acc, const float *lse_acc, void *o, const int64_t os[3],
+                           int dtype, float *lse, int batch, int hq, int64_t n, int hd,
+                           hipStream_t s) {
+  const int64_t rows = static_cast<int64_t>(batch) * hq * n;
+  if (rows == 0) return hipSuccess;
+  const int64_t th = rows * (hd / 4);
+  dim3 gr(blocks_for(th)), bl(NT);
+  const bool bf = dtype == 1;
+  if (hd == 128 && bf)
+    hipLaunchKernelGGL((finalize_kernel<128, true>), gr, bl, 0, s, o_acc, lse_acc, o, os[0], os[1], os[2], lse, hq, n, rows);
+  else if (hd == 128)
+    hipLaunchKernelGGL((finalize_kernel<128, false>), gr, bl, 0, s, o_acc, lse_acc, o, os[0], os[1], os[2], lse, hq, n, rows);
+  else if (bf)
+    hipLaunchKernelGGL((finalize_kernel<64, true>), gr, bl, 0, s, o_acc, lse_acc, o, os[0], os[1], os[2], lse, hq, n, rows);
+  else
+    hipLaunchKernelGGL((finalize_kernel<64, false>), gr, bl, 0, s, o_acc, lse_acc, o, os[0], os[1], os[2], lse, hq, n, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_rows(void *x, const int64_t strides[3], int dtype, int batch, int64_t n,
+                            int heads, int hd, float *lse, hipStream_t s) {
+  const int esize = dtype == 1 ? 2 : 4;
+  const int row_bytes = hd * esize;
+  const int64_t rows = static_cast<int64_t>(batch) * n * heads;
+  if (rows == 0) return hipSuccess;
+  const int64_t th = rows * (row_bytes / 16);
+  hipLaunchKernelGGL(zero_rows_kernel, dim3(blocks_for(th)), dim3(NT), 0, s,
+                     static_cast<char *>(x), strides[0], strides[1], strides[2], esize, heads, n,
+                     row_bytes, lse, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pre(const BwdArgs &a, int dtype, int hd, hipStream_t s) {
+  const int64_t rows = static_cast<int64_t>(a.g.batch) * a.g.hq * a.g.seqlen;
+  if (rows == 0) return hipSuccess;
+  dim3 gr(blocks_for(rows)), bl(NT);
+  const bool bf = dtype == 1;
+  if (hd == 128 && bf)
+    hipLaunchKernelGGL((bwd_pre_kernel<128, true>), gr, bl, 0, s, a);
+  else if (hd == 128)
+    hipLaunchKernelGGL((bwd_pre_kernel<128, false>), gr, bl, 0, s, a);
+  else if (bf)
+    hipLaunchKernelGGL((bwd_pre_kernel<64, true>), gr, bl, 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_pre_kernel<64, false>), gr, bl, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace dfa

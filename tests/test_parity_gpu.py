@@ -1,0 +1,225 @@
+"""GPU parity: the HIP library through the C ABI against the fp64 oracle on
+the same seeded inputs, element by element, at sizes that span several tiles
+and a ragged tail; plus edge cases and run-to-run determinism."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import schedule_ref as sr
+from tests.parity_util import (bhnd, check_grad, check_out, kv_rows_of, rows_of, to_np)
+
+pytestmark = pytest.mark.gpu
+
+RING, BAL, STR = sr.RING, sr.BALANCED, sr.STRIPED
+
+
+@pytest.fixture(scope="module")
+def dfa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import long_context_sequence_dfa_amd as m
+    from long_context_sequence_dfa_amd import binding
+    binding.lib()
+    return m
+
+
+def make(seed, B, N, Hq, Hkv, D, dtype, qkv_scale=None):
+    from long_context_sequence_dfa_amd import inputs
+    q, k, v, do = inputs.workload_tensors(seed, B, N, Hq, Hkv, D, dtype, qkv_scale, with_do=True)
+    dev = torch.device("cuda:0")
+    t = tuple(inputs.to_torch(x, dtype, dev) for x in (q, k, v, do))
+    return (q, k, v, do), t
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------- workload 1
+def test_ring_fp32_blocks_merge_and_full(dfa):
+    """N=1024, d=64, one head, fp32, contiguous ring with P=4: every block's
+    partial, the step-order merge per rank, and the full forward."""
+    say("case: ring fp32 N=1024 d=64 P=4 blocks/merge/full")
+    N, D, P = 1024, 64, 4
+    (q, k, v, do), (tq, tk, tv, tdo) = make(1001, 1, N, 1, 1, D, "f32")
+    scale = 1 / np.sqrt(D)
+    blocks = dfa.dfa_schedule_build(RING, N, P)
+    ro, rl = oracle.attn_rows(q, k, v, scale)
+    for r in range(P):
+        rb = blocks[blocks[:, 0] == r]
+        acc_o = torch.zeros((1, 1, N // P, D), dtype=torch.float32, device="cuda")
+        acc_l = torch.full((1, 1, N // P), float("-inf"), device="cuda")
+        for b in rb:  # step order
+            op, lp = dfa.dfa_attn_block_fwd(tq, tk, tv, b)
+            torch.cuda.synchronize()
+            xo, xl = oracle.block_partial(q, k, v, scale, *b[3:8])
+            check_out(to_np(op), xo, to_np(lp), xl, "f32", f"block {b[:3]}")
+            dfa.dfa_lse_merge(acc_o, acc_l, op, lp)
+        torch.cuda.synchronize()
+        rows = slice(r * N // P, (r + 1) * N // P)
+        check_out(to_np(acc_o), ro[:, :, rows], to_np(acc_l), rl[:, :, rows], "f32", f"rank {r}")
+    for mode in (dfa.DFA_FWD_FUSED, dfa.DFA_FWD_STEPWISE):
+        o, lse = dfa.dfa_attn_fwd(tq, tk, tv, blocks, mode)
+        torch.cuda.synchronize()
+        check_out(bhnd(to_np(o)), ro, to_np(lse), rl, "f32", f"fwd mode {mode}")
+    dq, dk, dv = dfa.dfa_attn_bwd(tq, tk, tv, o, tdo, lse, blocks)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = oracle.attn_grads(q, k, v, do, scale)
+    for n, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        check_grad(bhnd(to_np(g)), r, None, "f32", n)
+
+
+# ------------------------------------------------------------ bf16 matrix
+CASES = [
+    # kind, N, P, B, Hq, Hkv, D, subset rank
+    (BAL, 1024, 4, 1, 2, 2, 128, None),
+    (BAL, 1000, 4, 2, 4, 2, 128, None),     # ragged chunks (125 rows)
+    (RING, 768, 3, 2, 2, 1, 64, None),
+    (RING, 640, 5, 1, 3, 3, 128, None),
+    (STR, 1024, 8, 1, 2, 2, 128, None),
+    (STR, 1024, 8, 1, 4, 1, 128, 0),        # rank 0's share (diag offsets 0 and -1)
+    (STR, 1152, 16, 1, 2, 2, 64, 15),       # last rank's share
+    (BAL, 2048, 8, 1, 2, 1, 64, 3),         # one folded rank
+    (BAL, 96, 1, 1, 1, 1, 128, None),       # P = 1: one diagonal block
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(str(x) for x in c))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_forward_backward_parity(dfa, case, dtype):
+    kind, N, P, B, Hq, Hkv, D, sub = case
+    if dtype == "f32" and (N > 1024 or Hq > 2):
+        pytest.skip("fp32 path covered on the smaller cases")
+    say(f"case: {sr.KIND_NAMES[kind]} N={N} P={P} B={B} Hq={Hq} Hkv={Hkv} D={D} rank={sub} {dtype}")
+    (q, k, v, do), (tq, tk, tv, tdo) = make(2000 + N + P, B, N, Hq, Hkv, D, dtype)
+    scale = 1 / np.sqrt(D)
+    blocks = dfa.dfa_schedule_build(kind, N, P)
+    if sub is not None:
+        blocks = blocks[blocks[:, 0] == sub]
+    rows, krows = rows_of(blocks), kv_rows_of(blocks)
+    ro, rl = oracle.attn_rows(q, k, v, scale, rows=rows)
+    outs = {}
+    for mode in (dfa.DFA_FWD_FUSED, dfa.DFA_FWD_STEPWISE):
+        o, lse = dfa.dfa_attn_fwd(tq, tk, tv, blocks, mode)
+        torch.cuda.synchronize()
+        go, gl = bhnd(to_np(o)), to_np(lse)
+        check_out(go[:, :, rows], ro, gl[:, :, rows], rl, dtype, f"mode {mode}")
+        other = np.setdiff1d(np.arange(N), rows)
+        assert np.all(go[:, :, other] == 0) and np.all(np.isneginf(gl[:, :, other]))
+        outs[mode] = (o, lse)
+    o, lse = outs[dfa.DFA_FWD_FUSED]
+    dq, dk, dv = dfa.dfa_attn_bwd(tq, tk, tv, o, tdo, lse, blocks)
+    torch.cuda.synchronize()
+    (rdq, rdk, rdv), (adq, adk, adv) = oracle.attn_grads(q, k, v, do, scale, rows=rows, with_abs=True)
+    gq, gk, gv = bhnd(to_np(dq)), bhnd(to_np(dk)), bhnd(to_np(dv))
+    check_grad(gq[:, :, rows], rdq, adq, dtype, "dq")
+    check_grad(gk[:, :, krows], rdk[:, :, krows], adk[:, :, krows], dtype, "dk")
+    check_grad(gv[:, :, krows], rdv[:, :, krows], adv[:, :, krows], dtype, "dv")
+    # rows no block touches are zero, including key rows of other ranks
+    for g, touched in ((gq, rows), (gk, krows), (gv, krows)):
+        assert np.all(g[:, :, np.setdiff1d(np.arange(N), touched)] == 0)
+
+
+def test_block_partials_bf16_with_empty_rows(dfa):
+    """A striped block whose key shard comes after the query shard (shifted
+    diagonal): local row 0 sees no key and must come out as (0, -inf)."""
+    say("case: striped bf16 block partials N=512 P=4")
+    N, P, D = 512, 4, 128
+    (q, k, v, _), (tq, tk, tv, _) = make(3001, 1, N, 2, 2, D, "bf16")
+    scale = 1 / np.sqrt(D)
+    blocks = dfa.dfa_schedule_build(STR, N, P)
+    for b in blocks[:8]:
+        op, lp = dfa.dfa_attn_block_fwd(tq, tk, tv, b)
+        torch.cuda.synchronize()
+        xo, xl = oracle.block_partial(q, k, v, scale, *b[3:8])
+        check_out(to_np(op), xo, to_np(lp), xl, "bf16", f"block {b[:3]}")
+        if b[2] > b[0]:
+            assert np.all(np.isneginf(to_np(lp)[:, :, 0]))
+
+
+def test_merge_kernel_against_oracle(dfa):
+    say("case: lse merge kernel")
+    rng = np.random.default_rng(5)
+    n, D = 1000, 128
+    ao, po = rng.standard_normal((n, D)), rng.standard_normal((n, D))
+    al, pl = rng.standard_normal(n) * 3, rng.standard_normal(n) * 3
+    al[:10] = -np.inf
+    pl[5:15] = -np.inf
+    ta, tla = torch.tensor(ao, dtype=torch.float32, device="cuda"), torch.tensor(al, dtype=torch.float32, device="cuda")
+    tp, tlp = torch.tensor(po, dtype=torch.float32, device="cuda"), torch.tensor(pl, dtype=torch.float32, device="cuda")
+    # the oracle gets the same fp32 values
+    ao32, al32 = ta.cpu().double().numpy(), tla.cpu().double().numpy()
+    po32, pl32 = tp.cpu().double().numpy(), tlp.cpu().double().numpy()
+    ro, rl = oracle.merge(np.stack([ao32, po32]), np.stack([al32, pl32]))
+    dfa.dfa_lse_merge(ta, tla, tp, tlp)
+    torch.cuda.synchronize()
+    # rows 0-9: -inf accumulator takes the part; rows 5-9 both empty stay (0, -inf)
+    check_out(to_np(ta), ro, to_np(tla), rl, "f32", "merge")
+
+
+def test_empty_block_list_and_tiny_sequences(dfa):
+    say("case: empty block list, N=1, N=8 striped")
+    (q, k, v, do), (tq, tk, tv, tdo) = make(3002, 1, 64, 2, 1, 64, "bf16")
+    empty = np.zeros((0, 10), dtype=np.int64)
+    o, lse = dfa.dfa_attn_fwd(tq, tk, tv, empty)
+    dq, dk, dv = dfa.dfa_attn_bwd(tq, tk, tv, o, tdo, lse, empty)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)
+    for kind, N, P in ((RING, 1, 1), (STR, 8, 4), (BAL, 8, 4), (STR, 4, 4)):
+        (q, k, v, do), (tq, tk, tv, tdo) = make(3003, 1, N, 2, 1, 128, "bf16")
+        blocks = dfa.dfa_schedule_build(kind, N, P)
+        o, lse = dfa.dfa_attn_fwd(tq, tk, tv, blocks)
+        dq, dk, dv = dfa.dfa_attn_bwd(tq, tk, tv, o, tdo, lse, blocks)
+        torch.cuda.synchronize()
+        scale = 1 / np.sqrt(128)
+        ro, rl = oracle.attn_rows(q, k, v, scale)
+        check_out(bhnd(to_np(o)), ro, to_np(lse), rl, "bf16", f"tiny {kind} {N} {P}")
+        (rdq, rdk, rdv), (a1, a2, a3) = oracle.attn_grads(q, k, v, do, scale, with_abs=True)
+        check_grad(bhnd(to_np(dq)), rdq, a1, "bf16", "dq")
+        check_grad(bhnd(to_np(dk)), rdk, a2, "bf16", "dk")
+        check_grad(bhnd(to_np(dv)), rdv, a3, "bf16", "dv")
+
+
+def test_deterministic_forward_and_backward(dfa):
+    """No atomics anywhere: two runs give identical bits."""
+    say("case: determinism N=2048 balanced P=8 GQA")
+    (q, k, v, do), (tq, tk, tv, tdo) = make(3004, 1, 2048, 8, 2, 128, "bf16")
+    blocks = dfa.dfa_schedule_build(BAL, 2048, 8)
+    o1, l1 = dfa.dfa_attn_fwd(tq, tk, tv, blocks)
+    g1 = dfa.dfa_attn_bwd(tq, tk, tv, o1, tdo, l1, blocks)
+    o2, l2 = dfa.dfa_attn_fwd(tq, tk, tv, blocks)
+    g2 = dfa.dfa_attn_bwd(tq, tk, tv, o2, tdo, l2, blocks)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_strided_views(dfa):
+    """Tensors that are views with non-packed strides ([B, H, N, d] storage
+    seen as [B, N, H, d])."""
+    say("case: strided views")
+    N, H, D = 512, 2, 128
+    (q, k, v, do), _ = make(3005, 1, N, H, H, D, "bf16")
+    dev = torch.device("cuda")
+
+    def strided(x):
+        t = torch.from_numpy(np.ascontiguousarray(x.transpose(0, 2, 1, 3))).to(torch.bfloat16).to(dev)
+        return t.permute(0, 2, 1, 3)  # logical [B, N, H, d], storage [B, H, N, d]
+
+    tq, tk, tv, tdo = strided(q), strided(k), strided(v), strided(do)
+    blocks = dfa.dfa_schedule_build(BAL, N, 2)
+    o = torch.empty_like(tq)  # same strides as q
+    o, lse = dfa.dfa_attn_fwd(tq, tk, tv, blocks, o=o)
+    dq, dk, dv = dfa.dfa_attn_bwd(tq, tk, tv, o, tdo, lse, blocks,
+                                  dq=torch.empty_like(tq), dk=torch.empty_like(tk), dv=torch.empty_like(tv))
+    torch.cuda.synchronize()
+    scale = 1 / np.sqrt(D)
+    ro, rl = oracle.attn_rows(q, k, v, scale)
+    check_out(bhnd(to_np(o)), ro, to_np(lse), rl, "bf16", "strided")
+    (rdq, rdk, rdv), (a1, a2, a3) = oracle.attn_grads(q, k, v, do, scale, with_abs=True)
+    check_grad(bhnd(to_np(dq)), rdq, a1, "bf16", "dq")
+    check_grad(bhnd(to_np(dk)), rdk, a2, "bf16", "dk")
+    check_grad(bhnd(to_np(dv)), rdv, a3, "bf16", "dv")
