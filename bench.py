@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark: causal attention forward+backward throughput on one MI355X.
+
+One step = dfa_attn_fwd (fused) + dfa_attn_bwd over the whole DistFlashAttn
+folded schedule (P = 8 virtual ranks) of a Llama-7B attention layer:
+batch 1, 32 heads, head_dim 128, N = 32768, bf16, Q/K/V iid N(0,1) scaled by
+1/sqrt(d), dO iid N(0,1).  Inputs are generated before timing and stay
+resident in HBM.
+
+Throughput counts causal-effective FLOPs over the exact visible pairs:
+4*d per pair forward (QK^T and PV) and 10*d per pair backward (the recompute
+of S plus dP, dV, dK, dQ).  The dominant kernel's roofline figure uses the
+same per-pair counts and the kernel's own launch duration, read from HIP
+events recorded on the library's stream around that kernel.
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "causal attention fwd+bwd TFLOP/s and % bf16 MFMA peak, Llama-7B shape N=32K"
+
+WORKLOADS = {
+    "llama7b-n32k-balanced-p8": dict(B=1, N=32768, Hq=32, Hkv=32, D=128, kind=1, P=8, seed=1003,
+                                     scaled=True, rank=None),
+    "llama7b-n131k-striped-p16-rank0": dict(B=1, N=131072, Hq=32, Hkv=32, D=128, kind=2, P=16,
+                                            seed=1004, scaled=False, rank=0),
+    "gqa-32-8-n256k-balanced-p32": dict(B=1, N=262144, Hq=32, Hkv=8, D=128, kind=1, P=32,
+                                        seed=1005, scaled=False, rank=None),
+}
+
+
+class HipEvents:
+    """Minimal HIP event timing through libamdhip64 (events on a given stream)."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        if self.h.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
+    def elapsed(self, a, b) -> float:
+        self.h.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        if self.h.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+
+def cpu_baseline(wl: dict, budget_s: float = 20.0) -> dict:
+    """The fp64 oracle on a bounded sample of the workload: forward and full
+    gradients of head 0 over the first n tokens (a complete causal
+    sub-problem: those rows see only keys < n), timed on the host cores."""
+    import numpy as np
+
+    import oracle
+    from long_context_sequence_dfa_amd import inputs
+    oracle.build(force=False)
+    D = wl["D"]
+    scale = 1.0 / math.sqrt(D)
+    qs = scale if wl["scaled"] else None
+    best = None
+    n = 1024
+    while True:
+        q = inputs.normal_tensor(wl["seed"], 0, (1, n, 1, D), "bf16", qs)
+        k = inputs.normal_tensor(wl["seed"], 1, (1, n, 1, D), "bf16", qs)
+        v = inputs.normal_tensor(wl["seed"], 2, (1, n, 1, D), "bf16", qs)
+        do = inputs.normal_tensor(wl["seed"], 3, (1, n, 1, D), "bf16")
+        t0 = time.perf_counter()
+        oracle.attn_rows(q, k, v, scale)
+        oracle.attn_grads(q, k, v, do, scale)
+        dt = time.perf_counter() - t0
+        pairs = n * (n + 1) // 2
+        best = (n, dt, 14.0 * D * pairs / dt / 1e12)
+        if dt * 4.2 > budget_s or n >= 32768:  # next doubling would exceed the budget
+            break
+        n *= 2
+    n, dt, tflops = best
+    return {"value": tflops, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"head 0, first {n} tokens (complete causal prefix), fwd + full grads, "
+                      f"fp64, {dt:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama7b-n32k-balanced-p8", choices=sorted(WORKLOADS))
+    ap.add_argument("--mode", default="fused", choices=["fused", "stepwise"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus "
+              f"{args.gpus}); the schedules run as virtual ranks on one device.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import long_context_sequence_dfa_amd as dfa
+    from long_context_sequence_dfa_amd import binding, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    binding.lib()
+    wl = WORKLOADS[args.workload]
+    B, N, Hq, Hkv, D = wl["B"], wl["N"], wl["Hq"], wl["Hkv"], wl["D"]
+    dev = torch.device("cuda:0")
+    scale = 1.0 / math.sqrt(D)
+    qs = scale if wl["scaled"] else None
+    q, k, v, do = inputs.workload_tensors(wl["seed"], B, N, Hq, Hkv, D, "bf16", qs, with_do=True)
+    tq, tk, tv, tdo = (inputs.to_torch(x, "bf16", dev) for x in (q, k, v, do))
+    del q, k, v, do
+    blocks = dfa.dfa_schedule_build(wl["kind"], N, wl["P"])
+    if wl["rank"] is not None:
+        blocks = blocks[blocks[:, 0] == wl["rank"]]
+    pairs = int(blocks[:, 9].sum()) * B * Hq
+    fwd_flops = 4.0 * D * pairs
+    bwd_flops = 10.0 * D * pairs
+    mode = dfa.DFA_FWD_FUSED if args.mode == "fused" else dfa.DFA_FWD_STEPWISE
+    bal = dfa.dfa_schedule_balance(dfa.dfa_schedule_build(wl["kind"], N, wl["P"]), wl["P"])
+
+    o = torch.empty_like(tq)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
+    desc = dfa.make_desc(tq, tk, tv, o)
+    op_f = dfa.DFA_OP_FWD_FUSED if mode == dfa.DFA_FWD_FUSED else dfa.DFA_OP_FWD_STEPWISE
+    ws_f = torch.empty(max(dfa.dfa_workspace_size(desc, blocks, op_f), 256), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(max(dfa.dfa_workspace_size(desc, blocks, dfa.DFA_OP_BWD), 256), dtype=torch.uint8,
+                       device=dev)
+    stream = torch.cuda.current_stream()
+    ev = HipEvents()
+    marks = [[ev.create() for _ in range(3)] for _ in range(args.steps)]
+
+    def step(m=None):
+        if m is not None:
+            ev.h.hipEventRecord(m[0], ctypes.c_void_p(stream.cuda_stream))
+        dfa.dfa_attn_fwd(tq, tk, tv, blocks, mode, o=o, lse=lse, workspace=ws_f)
+        if m is not None:
+            ev.h.hipEventRecord(m[1], ctypes.c_void_p(stream.cuda_stream))
+        dfa.dfa_attn_bwd(tq, tk, tv, o, tdo, lse, blocks, dq=dq, dk=dk, dv=dv, workspace=ws_b)
+        if m is not None:
+            ev.h.hipEventRecord(m[2], ctypes.c_void_p(stream.cuda_stream))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(marks[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    fwd_ms = [ev.elapsed(m[0], m[1]) for m in marks]
+    bwd_ms = [ev.elapsed(m[1], m[2]) for m in marks]
+    ms_step = elapsed * 1e3 / args.steps
+    total_flops = (fwd_flops + bwd_flops) * args.steps
+    value = total_flops / elapsed / 1e12
+    fwd_avg, bwd_avg = float(np.mean(fwd_ms)), float(np.mean(bwd_ms))
+
+    # dominant kernel: the fused forward kernel is the only kernel of
+    # dfa_attn_fwd besides a small table upload; report it when it is the
+    # larger share, else the backward as one unit
+    if fwd_avg >= bwd_avg:
+        dom, dom_ms, dom_flops = "attn_fwd_bf16 (fused)", fwd_avg, fwd_flops
+    else:
+        dom, dom_ms, dom_flops = "attn_bwd (dq + dkdv)", bwd_avg, bwd_flops
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None}
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "fwd_ms": fwd_avg,
+        "bwd_ms": bwd_avg,
+        "fwd_tflops": fwd_flops / (fwd_avg * 1e-3) / 1e12,
+        "bwd_tflops": bwd_flops / (bwd_avg * 1e-3) / 1e12,
+        "idle_bubble_ratio": bal["bubble"],
+        "comm_latency_ms": 0.0,
+        "config": {"workload": args.workload, "global_batch": B, "seq_len": N, "heads_q": Hq,
+                   "heads_kv": Hkv, "head_dim": D,
+                   "schedule": {0: "ring", 1: "balanced", 2: "striped"}[wl["kind"]],
+                   "virtual_ranks": wl["P"], "rank_share": wl["rank"], "mode": args.mode,
+                   "parallelism": "none: virtual ranks on one GPU"},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
