@@ -34,14 +34,17 @@ constexpr int DQ_BK = 64;
 
 template <int HD>
 __global__ __launch_bounds__(NT, 2) void dq_bf16_kernel(BwdArgs a) {
-  constexpr int PITCH = HD * 2 + 32;
+  constexpr int PITCH = HD * 2 + 32;  // K tile: transposing reads of 4 rows conflict-free
+  constexpr int VPITCH = HD * 2 + 16; // V tile: b128 reads of 16 rows conflict-free
   constexpr int TILEB = DQ_BK * PITCH;
+  constexpr int BUFB = TILEB + DQ_BK * VPITCH;
   constexpr int KS = HD / 16, DT = HD / 32, CH = HD / 8, RPP = NT / CH, NP = DQ_BK / RPP;
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILEB];
+  __shared__ __attribute__((aligned(16))) char smem[2 * BUFB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, c32 = lane & 31;
   const Geom &G = a.g;
+  const float c = G.scale_log2;
   const int BH = G.batch * G.hq;
   const int64_t bid = blockIdx.x;
   const int bh = static_cast<int>(bid % BH);
@@ -54,14 +57,14 @@ __global__ __launch_bounds__(NT, 2) void dq_bf16_kernel(BwdArgs a) {
 
   const char *kb = static_cast<const char *>(a.k) + 2 * (b * G.ks[0] + hk * G.ks[2]);
   const char *vb = static_cast<const char *>(a.v) + 2 * (b * G.vs[0] + hk * G.vs[2]);
+  const int64_t krs = 2 * G.ks[1] * seg.stride, vrs = 2 * G.vs[1] * seg.stride;
 
+  // rows past the piece read its last row; they are never stored
   bf16x8 qf[KS], df[KS];
-  float lse2 = 0.f, dd = 0.f;
   const int64_t row = i0w + c32;
   const bool valid = row < seg.len_q;
-  int64_t pos = 0;
-  if (valid) {
-    pos = seg.q_start + row * seg.stride;
+  const int64_t pos = seg.q_start + (valid ? row : seg.len_q - 1) * seg.stride;
+  {
     const char *qsrc = static_cast<const char *>(a.q) + 2 * (b * G.qs[0] + pos * G.qs[1] + h * G.qs[2]);
     const char *dsrc = static_cast<const char *>(a.dout) + 2 * (b * G.os[0] + pos * G.os[1] + h * G.os[2]);
 #pragma unroll
@@ -69,13 +72,10 @@ __global__ __launch_bounds__(NT, 2) void dq_bf16_kernel(BwdArgs a) {
       qf[ks] = __builtin_bit_cast(bf16x8, ld16(qsrc + (2 * ks + g) * 16));
       df[ks] = __builtin_bit_cast(bf16x8, ld16(dsrc + (2 * ks + g) * 16));
     }
-    const int64_t r = (static_cast<int64_t>(b) * G.hq + h) * G.seqlen + pos;
-    lse2 = a.lse[r] * kLog2e;
-    dd = a.dd[r];
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = df[ks] = bf16x8{};
   }
+  const int64_t lr = (static_cast<int64_t>(b) * G.hq + h) * G.seqlen + pos;
+  const float lse2 = a.lse[lr] * kLog2e;
+  const float dd = a.dd[lr];
 
   f32x16 acc[DT];
 #pragma unroll
@@ -102,26 +102,24 @@ __global__ __launch_bounds__(NT, 2) void dq_bf16_kernel(BwdArgs a) {
   }
   const int lrow = tid / CH, lch = tid % CH;
   u32x4 kr[NP], vr[NP];
+  // rows past the key piece re-read its last row; the mask zeroes them
   auto gload = [&](const Walk &w, int64_t t) {
+    const char *kp = kb + 2 * w.kv_start * G.ks[1] + lch * 16;
+    const char *vp = vb + 2 * w.kv_start * G.vs[1] + lch * 16;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const int64_t j = t * DQ_BK + lrow + p * RPP;
-      if (j < w.len_kv) {
-        const int64_t kp = w.kv_start + j * seg.stride;
-        kr[p] = ld16(kb + 2 * kp * G.ks[1] + lch * 16);
-        vr[p] = ld16(vb + 2 * kp * G.vs[1] + lch * 16);
-      } else {
-        kr[p] = u32x4{0, 0, 0, 0};
-        vr[p] = u32x4{0, 0, 0, 0};
-      }
+      int64_t j = t * DQ_BK + lrow + p * RPP;
+      j = j < w.len_kv ? j : w.len_kv - 1;
+      kr[p] = ld16(kp + j * krs);
+      vr[p] = ld16(vp + j * vrs);
     }
   };
   auto lstore = [&](int buf) {
-    char *kt = smem + buf * 2 * TILEB;
+    char *kt = smem + buf * BUFB;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       st16(kt + (lrow + p * RPP) * PITCH + lch * 16, kr[p]);
-      st16(kt + TILEB + (lrow + p * RPP) * PITCH + lch * 16, vr[p]);
+      st16(kt + TILEB + (lrow + p * RPP) * VPITCH + lch * 16, vr[p]);
     }
   };
   int64_t t = 0;
@@ -149,41 +147,48 @@ __global__ __launch_bounds__(NT, 2) void dq_bf16_kernel(BwdArgs a) {
 
     const int64_t j0 = t * DQ_BK;
     if (j0 <= i0w + 31 + cw.diag) {
-      const char *kt = smem + cur * 2 * TILEB;
+      const char *kt = smem + cur * BUFB;
       const char *vt = kt + TILEB;
       f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
       const int ro = kperm(c32) * PITCH + g * 16;
+      const int vo = kperm(c32) * VPITCH + g * 16;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 k0 = __builtin_bit_cast(bf16x8, ld16(kt + ro + ks * 32));
         const bf16x8 k1 = __builtin_bit_cast(bf16x8, ld16(kt + ro + 32 * PITCH + ks * 32));
-        const bf16x8 v0 = __builtin_bit_cast(bf16x8, ld16(vt + ro + ks * 32));
-        const bf16x8 v1 = __builtin_bit_cast(bf16x8, ld16(vt + ro + 32 * PITCH + ks * 32));
+        const bf16x8 v0 = __builtin_bit_cast(bf16x8, ld16(vt + vo + ks * 32));
+        const bf16x8 v1 = __builtin_bit_cast(bf16x8, ld16(vt + vo + 32 * VPITCH + ks * 32));
         s0 = mfma32(k0, qf[ks], s0);
         s1 = mfma32(k1, qf[ks], s1);
         p0 = mfma32(v0, df[ks], p0);
         p1 = mfma32(v1, df[ks], p1);
       }
-      const bool need_mask = (j0 + DQ_BK - 1 > i0w + cw.diag) || (j0 + DQ_BK > cw.len_kv);
-      const int64_t lim = row + cw.diag;
+      if ((j0 + DQ_BK - 1 > i0w + cw.diag) || (j0 + DQ_BK > cw.len_kv)) {
+        // local key j0 + jj is visible iff jj <= lim (32-bit)
+        const int64_t lim64 = row + cw.diag - j0, len64 = cw.len_kv - 1 - j0;
+        const int64_t m64 = lim64 < len64 ? lim64 : len64;
+        const int lim = static_cast<int>(m64 < -1 ? -1 : m64);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int jj = 16 * (i / 8) + 8 * g + (i % 8);
+          if (jj > lim) s0[i] = -INFINITY;
+          if (jj + 32 > lim) s1[i] = -INFINITY;
+        }
+      }
       bf16x8 dsb[4];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float s = (i < 16 ? s0[i] : s1[i - 16]);
-        const float dp = (i < 16 ? p0[i] : p1[i - 16]);
-        float p = fast_exp2(s * G.scale_log2 - lse2);
-        if (need_mask) {
-          const int64_t j = j0 + 32 * (i / 16) + 16 * ((i % 16) / 8) + 8 * g + (i % 8);
-          if (j > lim || j >= cw.len_kv) p = 0.f;
-        }
-        dsb[i / 8][i % 8] = static_cast<__bf16>(p * (dp - dd));
+      for (int i = 0; i < 16; ++i) {
+        const float pa = fast_exp2(__builtin_fmaf(s0[i], c, -lse2));
+        const float pc = fast_exp2(__builtin_fmaf(s1[i], c, -lse2));
+        dsb[i / 8][i % 8] = static_cast<__bf16>(pa * (p0[i] - dd));
+        dsb[2 + i / 8][i % 8] = static_cast<__bf16>(pc * (p1[i] - dd));
       }
       // dQ^T += K^T dS^T: A = K^T (d x 16 keys) read transposed from the K tile
       const int krow = 8 * g + (lane & 15) / 4;
       const int kcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const char *kp = kt + (16 * kk + krow) * PITCH + kcol * 2;
+        const char *kp = kt + (16 * kk + krow) * PITCH + kcol * 2;  // kt: current K tile
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const bf16x4 lo = lds_read_tr(kp + dt * 64);
@@ -218,7 +223,7 @@ constexpr int KV_BQ = 64;          // query rows per streamed tile
 
 template <int HD>
 __global__ __launch_bounds__(NT, 1) void dkdv_bf16_kernel(BwdArgs a) {
-  constexpr int PITCH = HD * 2 + 32;
+  constexpr int PITCH = HD * 2 + 32;  // transposing reads of 4 rows conflict-free
   constexpr int TILEB = KV_BQ * PITCH;
   constexpr int BUFB = 2 * TILEB + 2 * KV_BQ * 4;  // Q, dO, lse*log2e, D
   constexpr int KS = HD / 16, DT = HD / 32, CH = HD / 8, RPP = NT / CH, NP = KV_BQ / RPP;
@@ -227,6 +232,7 @@ __global__ __launch_bounds__(NT, 1) void dkdv_bf16_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, c32 = lane & 31;
   const Geom &G = a.g;
+  const float c = G.scale_log2;
   const int BH = G.batch * G.hkv;
   const int64_t bid = blockIdx.x;
   const int bh = static_cast<int>(bid % BH);
@@ -238,11 +244,11 @@ __global__ __launch_bounds__(NT, 1) void dkdv_bf16_kernel(BwdArgs a) {
   const int64_t col = j0w + c32;  // this lane's key row
   const bool valid = col < seg.len_kv;
 
-  // K and V as B operands of S = Q K^T and dP = dO V^T
+  // K and V as B operands of S = Q K^T and dP = dO V^T; rows past the key
+  // piece read its last row and are never stored
   bf16x8 kf[KS], vf[KS];
-  int64_t pos = 0;
-  if (valid) {
-    pos = seg.kv_start + col * seg.stride;
+  const int64_t pos = seg.kv_start + (valid ? col : seg.len_kv - 1) * seg.stride;
+  {
     const char *ksrc = static_cast<const char *>(a.k) + 2 * (b * G.ks[0] + pos * G.ks[1] + hk * G.ks[2]);
     const char *vsrc = static_cast<const char *>(a.v) + 2 * (b * G.vs[0] + pos * G.vs[1] + hk * G.vs[2]);
 #pragma unroll
@@ -250,9 +256,6 @@ __global__ __launch_bounds__(NT, 1) void dkdv_bf16_kernel(BwdArgs a) {
       kf[ks] = __builtin_bit_cast(bf16x8, ld16(ksrc + (2 * ks + g) * 16));
       vf[ks] = __builtin_bit_cast(bf16x8, ld16(vsrc + (2 * ks + g) * 16));
     }
-  } else {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kf[ks] = vf[ks] = bf16x8{};
   }
   f32x16 dk[DT], dv[DT];
 #pragma unroll
@@ -292,33 +295,26 @@ __global__ __launch_bounds__(NT, 1) void dkdv_bf16_kernel(BwdArgs a) {
   int64_t t = cw.t0;
 
   const int lrow = tid / CH, lch = tid % CH;
+  const int64_t qrs = 2 * G.qs[1] * seg.stride, ors = 2 * G.os[1] * seg.stride;
   u32x4 qr[NP], dr[NP];
   float lsr = 0.f, ddr = 0.f;
+  // rows past the query piece re-read its last row; LSE = +inf gives them P = 0
   auto gload = [&](const Walk &w, int64_t tt) {
-    const char *qb = static_cast<const char *>(a.q) + 2 * (b * G.qs[0] + w.h * G.qs[2]);
-    const char *db = static_cast<const char *>(a.dout) + 2 * (b * G.os[0] + w.h * G.os[2]);
+    const char *qb = static_cast<const char *>(a.q) + 2 * (b * G.qs[0] + w.q_start * G.qs[1] + w.h * G.qs[2]) + lch * 16;
+    const char *db = static_cast<const char *>(a.dout) + 2 * (b * G.os[0] + w.q_start * G.os[1] + w.h * G.os[2]) + lch * 16;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const int64_t i = tt * KV_BQ + lrow + p * RPP;
-      if (i < w.len_q) {
-        const int64_t qp = w.q_start + i * seg.stride;
-        qr[p] = ld16(qb + 2 * qp * G.qs[1] + lch * 16);
-        dr[p] = ld16(db + 2 * qp * G.os[1] + lch * 16);
-      } else {
-        qr[p] = u32x4{0, 0, 0, 0};
-        dr[p] = u32x4{0, 0, 0, 0};
-      }
+      int64_t i = tt * KV_BQ + lrow + p * RPP;
+      i = i < w.len_q ? i : w.len_q - 1;
+      qr[p] = ld16(qb + i * qrs);
+      dr[p] = ld16(db + i * ors);
     }
     if (tid < KV_BQ) {
       const int64_t i = tt * KV_BQ + tid;
-      if (i < w.len_q) {
-        const int64_t r = (static_cast<int64_t>(b) * G.hq + w.h) * G.seqlen + w.q_start + i * seg.stride;
-        lsr = a.lse[r] * kLog2e;
-        ddr = a.dd[r];
-      } else {
-        lsr = INFINITY;  // rows past the piece contribute P = 0
-        ddr = 0.f;
-      }
+      const int64_t ic = i < w.len_q ? i : w.len_q - 1;
+      const int64_t r = (static_cast<int64_t>(b) * G.hq + w.h) * G.seqlen + w.q_start + ic * seg.stride;
+      lsr = i < w.len_q ? a.lse[r] * kLog2e : INFINITY;
+      ddr = a.dd[r];
     }
   };
   auto lstore = [&](int buf) {
@@ -340,6 +336,10 @@ __global__ __launch_bounds__(NT, 1) void dkdv_bf16_kernel(BwdArgs a) {
     lstore(0);
   }
   __syncthreads();
+  const int ro = kperm(c32) * PITCH + g * 16;
+  const int trow = 8 * g + (lane & 15) / 4;
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int toff = trow * PITCH + tcol * 2;
   while (gi < ngrp) {
     int gn = gi, kn = k;
     int64_t tn = t + 1;
@@ -359,60 +359,51 @@ __global__ __launch_bounds__(NT, 1) void dkdv_bf16_kernel(BwdArgs a) {
       const char *dt_ = qt + TILEB;
       const float *lt = reinterpret_cast<const float *>(qt + 2 * TILEB);
       const float *ddt = lt + KV_BQ;
-      f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
-      const int ro = kperm(c32) * PITCH + g * 16;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 q0 = __builtin_bit_cast(bf16x8, ld16(qt + ro + ks * 32));
-        const bf16x8 q1 = __builtin_bit_cast(bf16x8, ld16(qt + ro + 32 * PITCH + ks * 32));
-        const bf16x8 d0 = __builtin_bit_cast(bf16x8, ld16(dt_ + ro + ks * 32));
-        const bf16x8 d1 = __builtin_bit_cast(bf16x8, ld16(dt_ + ro + 32 * PITCH + ks * 32));
-        s0 = mfma32(q0, kf[ks], s0);
-        s1 = mfma32(q1, kf[ks], s1);
-        p0 = mfma32(d0, vf[ks], p0);
-        p1 = mfma32(d1, vf[ks], p1);
+      // key col is visible to local query qq (0..63 in the tile) iff qq >= lo
+      // (32-bit); rows past the piece carry LSE = +inf
+      const bool need_mask = qi0 + cw.diag < j0w + 31;
+      int lo = 0;
+      if (need_mask) {
+        const int64_t lo64 = col - cw.diag - qi0;
+        lo = static_cast<int>(lo64 > KV_BQ ? KV_BQ : lo64);
       }
-      // element i of s0/s1 is query row qi0 + 32*(i/16) + 16*((i%16)/8) + 8g + i%8
-      const bool need_mask = (qi0 + cw.diag < j0w + 31) || (qi0 + KV_BQ > cw.len_q);
-      bf16x8 pb[4], dsb[4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int qoff = 16 * kk + 8 * g;
-        const f32x4 la = *reinterpret_cast<const f32x4 *>(lt + qoff);
-        const f32x4 lb = *reinterpret_cast<const f32x4 *>(lt + qoff + 4);
-        const f32x4 da = *reinterpret_cast<const f32x4 *>(ddt + qoff);
-        const f32x4 db = *reinterpret_cast<const f32x4 *>(ddt + qoff + 4);
+      for (int mt = 0; mt < 2; ++mt) {  // two halves of 32 query rows
+        f32x16 s = f32x16{}, dpm = f32x16{};
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const int i = 8 * kk + w;
-          const float s = (i < 16 ? s0[i] : s1[i - 16]);
-          const float dp = (i < 16 ? p0[i] : p1[i - 16]);
-          const float l2 = w < 4 ? la[w] : lb[w - 4];
-          const float D = w < 4 ? da[w] : db[w - 4];
-          float p = fast_exp2(s * G.scale_log2 - l2);
-          if (need_mask) {
-            const int64_t qi = qi0 + qoff + w;
-            if (col > qi + cw.diag) p = 0.f;
-          }
-          pb[kk][w] = static_cast<__bf16>(p);
-          dsb[kk][w] = static_cast<__bf16>(p * (dp - D));
+        for (int ks = 0; ks < KS; ++ks) {
+          s = mfma32(__builtin_bit_cast(bf16x8, ld16(qt + ro + mt * 32 * PITCH + ks * 32)), kf[ks], s);
+          dpm = mfma32(__builtin_bit_cast(bf16x8, ld16(dt_ + ro + mt * 32 * PITCH + ks * 32)), vf[ks], dpm);
         }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS: A operands read transposed from LDS
-      const int trow = 8 * g + (lane & 15) / 4;
-      const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        // element i is query row qi0 + 32mt + 16(i/8) + 8g + i%8
+        bf16x8 pb[2], dsb[2];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const char *dp_ = dt_ + (16 * kk + trow) * PITCH + tcol * 2;
-        const char *qp_ = qt + (16 * kk + trow) * PITCH + tcol * 2;
+        for (int u = 0; u < 2; ++u) {
+          const int qoff = 32 * mt + 16 * u + 8 * g;
+          const f32x4 la = *reinterpret_cast<const f32x4 *>(lt + qoff);
+          const f32x4 lb = *reinterpret_cast<const f32x4 *>(lt + qoff + 4);
+          const f32x4 da = *reinterpret_cast<const f32x4 *>(ddt + qoff);
+          const f32x4 db = *reinterpret_cast<const f32x4 *>(ddt + qoff + 4);
 #pragma unroll
-        for (int dd_ = 0; dd_ < DT; ++dd_) {
-          const bf16x4 dlo = lds_read_tr(dp_ + dd_ * 64);
-          const bf16x4 dhi = lds_read_tr(dp_ + 4 * PITCH + dd_ * 64);
-          dv[dd_] = mfma32(cat8(dlo, dhi), pb[kk], dv[dd_]);
-          const bf16x4 qlo = lds_read_tr(qp_ + dd_ * 64);
-          const bf16x4 qhi = lds_read_tr(qp_ + 4 * PITCH + dd_ * 64);
-          dk[dd_] = mfma32(cat8(qlo, qhi), dsb[kk], dk[dd_]);
+          for (int w = 0; w < 8; ++w) {
+            const int i = 8 * u + w;
+            float p = fast_exp2(__builtin_fmaf(s[i], c, -(w < 4 ? la[w] : lb[w - 4])));
+            if (need_mask && qoff + w < lo) p = 0.f;
+            pb[u][w] = static_cast<__bf16>(p);
+            dsb[u][w] = static_cast<__bf16>(p * (dpm[i] - (w < 4 ? da[w] : db[w - 4])));
+          }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS: A operands read transposed from LDS
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int kk = 2 * mt + u;
+          const char *dp_ = dt_ + 16 * kk * PITCH + toff;
+          const char *qp_ = qt + 16 * kk * PITCH + toff;
+#pragma unroll
+          for (int e = 0; e < DT; ++e) {
+            dv[e] = mfma32(cat8(lds_read_tr(dp_ + e * 64), lds_read_tr(dp_ + 4 * PITCH + e * 64)), pb[u], dv[e]);
+            dk[e] = mfma32(cat8(lds_read_tr(qp_ + e * 64), lds_read_tr(qp_ + 4 * PITCH + e * 64)), dsb[u], dk[e]);
+          }
         }
       }
     }

@@ -21,9 +21,16 @@
 //    the B operand of O^T = V^T P^T, so P goes from accumulator to MFMA
 //    operand without touching LDS;
 //  * V^T operands come straight from the row-major V tile in LDS through
-//    ds_read_b64_tr_b16;
+//    ds_read_b64_tr_b16; the K and V tiles get different row pitches so that
+//    both the b128 reads of K and the transposing reads of V are free of
+//    bank conflicts;
 //  * K/V tiles are double-buffered in LDS; the next tile's global loads are
-//    issued before the current tile's MFMAs.
+//    issued before the current tile's MFMAs;
+//  * the vector ALU is the scarce unit next to the MFMAs, so the softmax is
+//    kept lean: one FMA folds scale, log2(e) and the max into the exponent,
+//    and the running output is rescaled only when a row's max grows by more
+//    than 2^8 (exact: every probability is taken against the same reference
+//    max as its row sum, and stays below 2^8).
 // Score arithmetic runs in the log2 domain: x = s * scale * log2(e).
 #include "device_util.h"
 #include "dfa_internal.h"
@@ -59,14 +66,17 @@ __device__ __forceinline__ BlockWalk block_walk(const FwdArgs &a, const QSeg &se
 
 template <int HD, int OUT>
 __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdArgs a) {
-  constexpr int PITCH = HD * 2 + 32;  // bytes per LDS row (pad: conflict-free reads)
-  constexpr int TILEB = BK * PITCH;   // bytes of one K or V tile
-  constexpr int KS = HD / 16;         // MFMA k-steps over head_dim
-  constexpr int DT = HD / 32;         // 32-row output tiles over head_dim
-  constexpr int CH = HD / 8;          // 16-byte chunks per row
-  constexpr int RPP = NT / CH;        // rows per load pass
-  constexpr int NP = BK / RPP;        // load passes per tile
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILEB];
+  constexpr int KP = HD * 2 + 16;   // K tile pitch: b128 reads of 16 rows are conflict-free
+  constexpr int VP = HD * 2 + 32;   // V tile pitch: transposing reads of 4 rows are conflict-free
+  constexpr int KB = BK * KP;
+  constexpr int BUF = KB + BK * VP;
+  constexpr int KS = HD / 16;       // MFMA k-steps over head_dim
+  constexpr int DT = HD / 32;       // 32-row output tiles over head_dim
+  constexpr int CH = HD / 8;        // 16-byte chunks per row
+  constexpr int RPP = NT / CH;      // rows per load pass
+  constexpr int NP = BK / RPP;      // load passes per tile
+  constexpr float TAU = 8.f;        // lazy rescale threshold (log2 units)
+  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, c32 = lane & 31;
@@ -90,24 +100,22 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int64_t i0 = qt * BQ;
   const int64_t i0w = i0 + wave * 32;
   const int64_t iend = (i0 + BQ < seg.len_q) ? i0 + BQ : seg.len_q;
+  const float c = G.scale_log2;
 
   const char *qb = static_cast<const char *>(a.q) + 2 * (b * G.qs[0] + h * G.qs[2]);
   const char *kb = static_cast<const char *>(a.k) + 2 * (b * G.ks[0] + hk * G.ks[2]);
   const char *vb = static_cast<const char *>(a.v) + 2 * (b * G.vs[0] + hk * G.vs[2]);
+  const int64_t krs = 2 * G.ks[1] * seg.stride, vrs = 2 * G.vs[1] * seg.stride;  // bytes per row
 
   // Q^T operand (B of S^T = K Q^T): lane holds Q[row][16ks + 8g .. +8].
+  // Rows past the piece read its last row (their outputs are never stored).
   bf16x8 qf[KS];
   {
-    const int64_t row = i0w + c32;
-    if (row < seg.len_q) {
-      const char *src = qb + 2 * (seg.q_start + row * seg.stride) * G.qs[1];
+    int64_t row = i0w + c32;
+    row = row < seg.len_q ? row : seg.len_q - 1;
+    const char *src = qb + 2 * (seg.q_start + row * seg.stride) * G.qs[1];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qf[ks] = __builtin_bit_cast(bf16x8, ld16(src + (2 * ks + g) * 16));
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[ks] = bf16x8{};
-    }
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ld16(src + (2 * ks + g) * 16));
   }
 
   f32x16 acc[DT];
@@ -127,26 +135,24 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   const int lrow = tid / CH, lch = tid % CH;
   u32x4 kr[NP], vr[NP];
+  // rows past the block's key piece re-read its last row; the mask zeroes them
   auto gload = [&](const BlockWalk &w, int64_t t) {
+    const char *kp = kb + 2 * w.kv_start * G.ks[1] + lch * 16;
+    const char *vp = vb + 2 * w.kv_start * G.vs[1] + lch * 16;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const int64_t j = t * BK + lrow + p * RPP;
-      if (j < w.len_kv) {
-        const int64_t pos = w.kv_start + j * seg.stride;
-        kr[p] = ld16(kb + 2 * pos * G.ks[1] + lch * 16);
-        vr[p] = ld16(vb + 2 * pos * G.vs[1] + lch * 16);
-      } else {
-        kr[p] = u32x4{0, 0, 0, 0};
-        vr[p] = u32x4{0, 0, 0, 0};
-      }
+      int64_t j = t * BK + lrow + p * RPP;
+      j = j < w.len_kv ? j : w.len_kv - 1;
+      kr[p] = ld16(kp + j * krs);
+      vr[p] = ld16(vp + j * vrs);
     }
   };
   auto lstore = [&](int buf) {
-    char *kt = smem + buf * 2 * TILEB;
+    char *kt = smem + buf * BUF;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      st16(kt + (lrow + p * RPP) * PITCH + lch * 16, kr[p]);
-      st16(kt + TILEB + (lrow + p * RPP) * PITCH + lch * 16, vr[p]);
+      st16(kt + (lrow + p * RPP) * KP + lch * 16, kr[p]);
+      st16(kt + KB + (lrow + p * RPP) * VP + lch * 16, vr[p]);
     }
   };
 
@@ -158,6 +164,10 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
   __syncthreads();
 
+  const int kr0 = kperm(c32) * KP + g * 16;
+  const int vrow = 8 * g + (lane & 15) / 4;
+  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int voff = vrow * VP + vcol * 2;
   while (k < nblk) {
     // next (block, tile)
     int kn = k;
@@ -178,67 +188,64 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdArgs a) {
     // ---- compute the current tile ----
     const int64_t j0 = t * BK;
     if (j0 <= i0w + 31 + cw.diag) {  // some row of this wave sees a key of the tile
-      const char *kt = smem + cur * 2 * TILEB;
-      const char *vt = kt + TILEB;
+      const char *kt = smem + cur * BUF;
+      const char *vt = kt + KB;
       f32x16 s0 = f32x16{}, s1 = f32x16{};
-      const char *ka0 = kt + kperm(c32) * PITCH + g * 16;
-      const char *ka1 = ka0 + 32 * PITCH;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 a0 = __builtin_bit_cast(bf16x8, ld16(ka0 + ks * 32));
-        bf16x8 a1 = __builtin_bit_cast(bf16x8, ld16(ka1 + ks * 32));
-        s0 = mfma32(a0, qf[ks], s0);
-        s1 = mfma32(a1, qf[ks], s1);
+        s0 = mfma32(__builtin_bit_cast(bf16x8, ld16(kt + kr0 + ks * 32)), qf[ks], s0);
+        s1 = mfma32(__builtin_bit_cast(bf16x8, ld16(kt + kr0 + 32 * KP + ks * 32)), qf[ks], s1);
       }
-      float x[32];
+      // element i of s0 / s1 is key j0 + 32*(i/16) + 16*((i%16)/8) + 8g + i%8
+      if ((j0 + BK - 1 > i0w + cw.diag) || (j0 + BK > cw.len_kv)) {
+        // 32-bit local offsets: key j0 + jj is visible iff jj <= lim
+        const int64_t lim64 = i0w + c32 + cw.diag - j0;
+        const int64_t len64 = cw.len_kv - 1 - j0;
+        const int lim = static_cast<int>(lim64 < len64 ? (lim64 < -1 ? -1 : lim64) : (len64 < -1 ? -1 : len64));
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        x[i] = s0[i] * G.scale_log2;
-        x[16 + i] = s1[i] * G.scale_log2;
-      }
-      const bool need_mask = (j0 + BK - 1 > i0w + cw.diag) || (j0 + BK > cw.len_kv);
-      if (need_mask) {
-        const int64_t lim = i0w + c32 + cw.diag;  // last visible key of this lane's row
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const int64_t j = j0 + 32 * (i / 16) + 16 * ((i % 16) / 8) + 8 * g + (i % 8);
-          if (j > lim || j >= cw.len_kv) x[i] = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const int jj = 16 * (i / 8) + 8 * g + (i % 8);
+          if (jj > lim) s0[i] = -INFINITY;
+          if (jj + 32 > lim) s1[i] = -INFINITY;
         }
       }
-      float mx = x[0];
+      float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-      for (int i = 1; i < 32; ++i) mx = fmaxf(mx, x[i]);
-      mx = fmaxf(mx, wave_swap32(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float psum = 0.f;
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+      mx = fmaxf(mx, wave_swap32(mx)) * c;
+      // raise the reference max only when it grows by more than TAU: P <= 2^TAU
+      if (__any(mx > m_run + TAU)) {
+        const float m_new = fmaxf(m_run, mx);
+        // 1 for rows whose max did not rise (also all-masked rows: no -inf - -inf);
+        // 0 when a row sees its first key
+        const float alpha = m_new > m_run ? fast_exp2(m_run - m_new) : 1.f;
+        l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        x[i] = fast_exp2(x[i] - m_use);
-        psum += x[i];
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+        m_run = m_new;
       }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      float psum = 0.f;
       bf16x8 pb[4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int w = 0; w < 8; ++w) pb[kk][w] = static_cast<__bf16>(x[kk * 8 + w]);
+      for (int i = 0; i < 16; ++i) {
+        const float p0 = fast_exp2(__builtin_fmaf(s0[i], c, -m_use));
+        const float p1 = fast_exp2(__builtin_fmaf(s1[i], c, -m_use));
+        psum += p0 + p1;
+        pb[i / 8][i % 8] = static_cast<__bf16>(p0);
+        pb[2 + i / 8][i % 8] = static_cast<__bf16>(p1);
+      }
+      l_run += psum;
       // O^T += V^T P^T: A = V^T rows (d) x 16 keys, read transposed from LDS
-      const int vrow = 8 * g + (lane & 15) / 4;
-      const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const char *vp = vt + (16 * kk + vrow) * PITCH + vcol * 2;
+        const char *vp = vt + 16 * kk * VP + voff;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          bf16x4 lo = lds_read_tr(vp + dt * 64);
-          bf16x4 hi = lds_read_tr(vp + 4 * PITCH + dt * 64);
+          const bf16x4 lo = lds_read_tr(vp + dt * 64);
+          const bf16x4 hi = lds_read_tr(vp + 4 * VP + dt * 64);
           acc[dt] = mfma32(cat8(lo, hi), pb[kk], acc[dt]);
         }
       }

@@ -52,3 +52,4 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t u) {
 }
 
 }  // namespace dfa
+

@@ -177,9 +177,11 @@ def test_empty_block_list_and_tiny_sequences(dfa):
         ro, rl = oracle.attn_rows(q, k, v, scale)
         check_out(bhnd(to_np(o)), ro, to_np(lse), rl, "bf16", f"tiny {kind} {N} {P}")
         (rdq, rdk, rdv), (a1, a2, a3) = oracle.attn_grads(q, k, v, do, scale, with_abs=True)
-        check_grad(bhnd(to_np(dq)), rdq, a1, "bf16", "dq")
-        check_grad(bhnd(to_np(dk)), rdk, a2, "bf16", "dk")
-        check_grad(bhnd(to_np(dv)), rdv, a3, "bf16", "dv")
+        # a mean over a few hundred cancelling elements is not a statistic;
+        # the elementwise bound still applies
+        check_grad(bhnd(to_np(dq)), rdq, a1, "bf16", "dq", check_mean=False)
+        check_grad(bhnd(to_np(dk)), rdk, a2, "bf16", "dk", check_mean=False)
+        check_grad(bhnd(to_np(dv)), rdv, a3, "bf16", "dv", check_mean=False)
 
 
 def test_deterministic_forward_and_backward(dfa):
