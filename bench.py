@@ -9,9 +9,11 @@ resident in HBM.
 
 Throughput counts causal-effective FLOPs over the exact visible pairs:
 4*d per pair forward (QK^T and PV) and 10*d per pair backward (the recompute
-of S plus dP, dV, dK, dQ).  The dominant kernel's roofline figure uses the
-same per-pair counts and the kernel's own launch duration, read from HIP
-events recorded on the library's stream around that kernel.
+of S plus dP, dV, dK, dQ).  Per kernel the algorithmic share is: forward
+4*d, dK/dV kernel 8*d (S, dP, dV, dK), dQ kernel 2*d (its recompute of S and
+dP is extra work and not counted).  The dominant kernel's roofline figure
+uses that share and the kernel's own average duration, read from HIP events
+recorded on the stream right before and after it (dfa_attn_bwd_ex marks).
 
 Prints ONE JSON line.
 """
@@ -68,6 +70,27 @@ class HipEvents:
         return float(ms.value)
 
 
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary
+    (profiles/traffic.txt: FETCH_SIZE + WRITE_SIZE scaled by a plain copy),
+    or None when absent or when the kernel source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        parts = line.split()
+        if len(parts) == 4 and parts[0] == kernel and parts[1] == workload:
+            src = os.path.join(ROOT, "long_context_sequence_dfa_amd", "csrc", parts[2].split(":")[0])
+            want = parts[2].split(":")[1]
+            if not os.path.exists(src):
+                return None
+            if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != want:
+                return None
+            return float(parts[3])
+    return None
+
+
 def cpu_baseline(wl: dict, budget_s: float = 20.0) -> dict:
     """The fp64 oracle on a bounded sample of the workload: forward and full
     gradients of head 0 over the first n tokens (a complete causal
@@ -110,6 +133,8 @@ def main() -> int:
     ap.add_argument("--workload", default="llama7b-n32k-balanced-p8", choices=sorted(WORKLOADS))
     ap.add_argument("--mode", default="fused", choices=["fused", "stepwise"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 1 GiB device copy first (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus "
@@ -152,44 +177,56 @@ def main() -> int:
     ws_b = torch.empty(max(dfa.dfa_workspace_size(desc, blocks, dfa.DFA_OP_BWD), 256), dtype=torch.uint8,
                        device=dev)
     stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
     ev = HipEvents()
-    marks = [[ev.create() for _ in range(3)] for _ in range(args.steps)]
+    # per step: fwd begin, fwd end, then the backward's marks
+    ev_all = [[ev.create() for _ in range(6)] for _ in range(args.steps)]
 
     def step(m=None):
         if m is not None:
-            ev.h.hipEventRecord(m[0], ctypes.c_void_p(stream.cuda_stream))
+            ev.h.hipEventRecord(m[0], sp)
         dfa.dfa_attn_fwd(tq, tk, tv, blocks, mode, o=o, lse=lse, workspace=ws_f)
+        marks = None
         if m is not None:
-            ev.h.hipEventRecord(m[1], ctypes.c_void_p(stream.cuda_stream))
-        dfa.dfa_attn_bwd(tq, tk, tv, o, tdo, lse, blocks, dq=dq, dk=dk, dv=dv, workspace=ws_b)
-        if m is not None:
-            ev.h.hipEventRecord(m[2], ctypes.c_void_p(stream.cuda_stream))
+            ev.h.hipEventRecord(m[1], sp)
+            marks = binding.DfaKernelMarks(m[2], m[3], m[4], m[5])
+        dfa.dfa_attn_bwd(tq, tk, tv, o, tdo, lse, blocks, dq=dq, dk=dk, dv=dv, workspace=ws_b,
+                         marks=marks)
 
+    if args.calibrate_copy:
+        # one plain device copy of known size: the scale for HBM byte counters
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(marks[i])
+        step(ev_all[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    fwd_ms = [ev.elapsed(m[0], m[1]) for m in marks]
-    bwd_ms = [ev.elapsed(m[1], m[2]) for m in marks]
+    per = {name: float(np.mean([ev.elapsed(m[a], m[b]) for m in ev_all]))
+           for name, a, b in (("fwd", 0, 1), ("bwd", 1, 5), ("bwd_pre", 2, 3), ("dq", 3, 4),
+                              ("dkdv", 4, 5))}
     ms_step = elapsed * 1e3 / args.steps
     total_flops = (fwd_flops + bwd_flops) * args.steps
     value = total_flops / elapsed / 1e12
-    fwd_avg, bwd_avg = float(np.mean(fwd_ms)), float(np.mean(bwd_ms))
+    fwd_avg, bwd_avg = per["fwd"], per["bwd"]
 
-    # dominant kernel: the fused forward kernel is the only kernel of
-    # dfa_attn_fwd besides a small table upload; report it when it is the
-    # larger share, else the backward as one unit
-    if fwd_avg >= bwd_avg:
-        dom, dom_ms, dom_flops = "attn_fwd_bf16 (fused)", fwd_avg, fwd_flops
-    else:
-        dom, dom_ms, dom_flops = "attn_bwd (dq + dkdv)", bwd_avg, bwd_flops
+    # the dominant kernel by time, with its algorithmic FLOP share
+    kernels = {"attn_fwd_bf16_fused": (per["fwd"], fwd_flops),
+               "attn_bwd_dq_bf16": (per["dq"], 2.0 * D * pairs),
+               "attn_bwd_dkdv_bf16": (per["dkdv"], 8.0 * D * pairs)}
+    dom = max(kernels, key=lambda n: kernels[n][0])
+    dom_ms, dom_flops = kernels[dom]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None}
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": stored_traffic(dom, args.workload), "launch_ms": dom_ms,
+                "algorithmic_flop": dom_flops}
 
     result = {
         "metric": METRIC,
@@ -207,6 +244,7 @@ def main() -> int:
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "fwd_ms": fwd_avg,
         "bwd_ms": bwd_avg,
+        "kernel_ms": {k_: per[k_] for k_ in ("fwd", "bwd_pre", "dq", "dkdv")},
         "fwd_tflops": fwd_flops / (fwd_avg * 1e-3) / 1e12,
         "bwd_tflops": bwd_flops / (bwd_avg * 1e-3) / 1e12,
         "idle_bubble_ratio": bal["bubble"],

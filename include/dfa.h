@@ -236,6 +236,32 @@ dfa_status dfa_attn_bwd(const dfa_attn_desc *d, const dfa_block *blocks, int64_t
                         void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Optional timing marks for dfa_attn_bwd_ex.  Each non-NULL member is a
+ * hipEvent_t (passed as void*) created by the caller; the call records it on
+ * its stream right before the named kernel is launched, or (end) right after
+ * its last launch.  Recording changes no result and skips no work.  The
+ * backward launches, in order: D = rowsum(dO*O), the dQ kernel, the dK/dV
+ * kernel.
+ */
+typedef struct dfa_kernel_marks {
+  void *pre_begin;
+  void *dq_begin;
+  void *dkdv_begin;
+  void *end;
+} dfa_kernel_marks;
+
+/*
+ * dfa_attn_bwd_ex -- dfa_attn_bwd plus per-kernel timing marks (marks may be
+ * NULL, which makes it identical to dfa_attn_bwd).  An event that fails to
+ * record returns DFA_E_HIP after the work is enqueued.
+ */
+dfa_status dfa_attn_bwd_ex(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n_blocks,
+                           const void *q, const void *k, const void *v, const void *o,
+                           const void *d_o, const float *lse, void *dq, void *dk, void *dv,
+                           void *workspace, size_t ws_bytes, const dfa_kernel_marks *marks,
+                           void *stream);
+
+/*
  * dfa_workspace_size -- bytes of workspace `op` (DFA_OP_*) needs for this
  * descriptor and block list.  Pure host computation.
  */

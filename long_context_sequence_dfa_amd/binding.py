@@ -25,7 +25,8 @@ DFA_FWD_FUSED, DFA_FWD_STEPWISE = 0, 1
 DFA_OP_FWD_FUSED, DFA_OP_FWD_STEPWISE, DFA_OP_BWD = 0, 1, 2
 
 EXPORTED = ("dfa_schedule_build", "dfa_schedule_balance", "dfa_attn_block_fwd", "dfa_lse_merge",
-            "dfa_attn_fwd", "dfa_attn_bwd", "dfa_workspace_size", "dfa_status_string")
+            "dfa_attn_fwd", "dfa_attn_bwd", "dfa_attn_bwd_ex", "dfa_workspace_size",
+            "dfa_status_string")
 BLOCK_FIELDS = ("rank", "step", "kv_rank", "q_start", "kv_start", "len_q", "len_kv", "stride",
                 "diag_offset", "pairs")
 
@@ -46,6 +47,11 @@ class DfaAttnDesc(ctypes.Structure):
 class DfaBalance(ctypes.Structure):
     _fields_ = [("total_pairs", ctypes.c_int64), ("busy_slots", ctypes.c_int64),
                 ("bubble", ctypes.c_double), ("eta_blocks", ctypes.c_double)]
+
+
+class DfaKernelMarks(ctypes.Structure):
+    _fields_ = [("pre_begin", ctypes.c_void_p), ("dq_begin", ctypes.c_void_p),
+                ("dkdv_begin", ctypes.c_void_p), ("end", ctypes.c_void_p)]
 
 
 class DfaError(RuntimeError):
@@ -74,6 +80,7 @@ def lib() -> ctypes.CDLL:
             L.dfa_lse_merge.argtypes = [i64, i32, p, p, p, p, p]
             L.dfa_attn_fwd.argtypes = [p, p, i64, i32, p, p, p, p, p, p, sz, p]
             L.dfa_attn_bwd.argtypes = [p, p, i64, p, p, p, p, p, p, p, p, p, p, sz, p]
+            L.dfa_attn_bwd_ex.argtypes = [p, p, i64, p, p, p, p, p, p, p, p, p, p, sz, p, p]
             L.dfa_workspace_size.argtypes = [p, p, i64, i32, ctypes.POINTER(sz)]
             L.dfa_status_string.argtypes = [i32]
             L.dfa_status_string.restype = ctypes.c_char_p
@@ -235,8 +242,9 @@ def dfa_attn_fwd(q, k, v, blocks, mode=DFA_FWD_FUSED, o=None, lse=None, workspac
 
 
 def dfa_attn_bwd(q, k, v, o, d_o, lse, blocks, dq=None, dk=None, dv=None, workspace=None,
-                 scale=None, stream=None):
-    """Gradients (dq, dk, dv) of the forward over the same block list."""
+                 scale=None, stream=None, marks=None):
+    """Gradients (dq, dk, dv) of the forward over the same block list.
+    ``marks``: optional DfaKernelMarks of hipEvent_t handles (dfa_attn_bwd_ex)."""
     import torch
     if d_o.stride() != o.stride():
         raise ValueError("d_o must have o's strides")
@@ -248,8 +256,11 @@ def dfa_attn_bwd(q, k, v, o, d_o, lse, blocks, dq=None, dk=None, dv=None, worksp
     desc = make_desc(q, k, v, o, scale)
     arr = _blocks_arg(blocks)
     ws, nbytes = _workspace(desc, arr, DFA_OP_BWD, q.device, workspace)
-    _check(lib().dfa_attn_bwd(ctypes.byref(desc), arr.ctypes.data_as(ctypes.c_void_p),
-                              arr.shape[0], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o),
-                              _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), nbytes,
-                              _stream(stream)), "dfa_attn_bwd")
+    args = (ctypes.byref(desc), arr.ctypes.data_as(ctypes.c_void_p), arr.shape[0], _ptr(q),
+            _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(ws), nbytes)
+    if marks is None:
+        _check(lib().dfa_attn_bwd(*args, _stream(stream)), "dfa_attn_bwd")
+    else:
+        _check(lib().dfa_attn_bwd_ex(*args, ctypes.byref(marks), _stream(stream)), "dfa_attn_bwd_ex")
     return dq, dk, dv

@@ -611,6 +611,16 @@ extern "C" dfa_status dfa_attn_bwd(const dfa_attn_desc *d, const dfa_block *bloc
                                    const void *o, const void *d_o, const float *lse, void *dq,
                                    void *dk, void *dv, void *workspace, size_t ws_bytes,
                                    void *stream) {
+  return dfa_attn_bwd_ex(d, blocks, n_blocks, q, k, v, o, d_o, lse, dq, dk, dv, workspace,
+                         ws_bytes, nullptr, stream);
+}
+
+extern "C" dfa_status dfa_attn_bwd_ex(const dfa_attn_desc *d, const dfa_block *blocks,
+                                      int64_t n_blocks, const void *q, const void *k,
+                                      const void *v, const void *o, const void *d_o,
+                                      const float *lse, void *dq, void *dk, void *dv,
+                                      void *workspace, size_t ws_bytes,
+                                      const dfa_kernel_marks *marks, void *stream) {
   dfa_status st = check_desc(d);
   if (st != DFA_OK) return st;
   if (!q || !k || !v || !o || !d_o || !lse || !dq || !dk || !dv) return DFA_E_NULL;
@@ -674,16 +684,24 @@ extern "C" dfa_status dfa_attn_bwd(const dfa_attn_desc *d, const dfa_block *bloc
   a.kvq = reinterpret_cast<const QRef *>(ws + L.kvq);
   a.kvtiles = reinterpret_cast<const Tile *>(ws + L.kvtiles);
   a.n_kvtiles = static_cast<int32_t>(kp.tiles.size());
+  bool mark_ok = true;
+  auto mark = [&](void *ev) {
+    if (ev && hipEventRecord(static_cast<hipEvent_t>(ev), s) != hipSuccess) mark_ok = false;
+  };
+  if (marks) mark(marks->pre_begin);
   st = hip_status(dfa::launch_bwd_pre(a, d->dtype, hd, s));
   if (st != DFA_OK) return st;
   const int64_t BHq = static_cast<int64_t>(d->batch) * d->heads_q;
   const int64_t BHkv = static_cast<int64_t>(d->batch) * d->heads_kv;
-  if (d->dtype == DFA_BF16) {
-    st = hip_status(dfa::launch_bwd_dq_bf16(a, hd, a.n_qtiles * BHq, s));
-    if (st != DFA_OK) return st;
-    return hip_status(dfa::launch_bwd_dkdv_bf16(a, hd, a.n_kvtiles * BHkv, s));
-  }
-  st = hip_status(dfa::launch_bwd_dq_f32(a, hd, a.n_qtiles * BHq, s));
+  const bool bf = d->dtype == DFA_BF16;
+  if (marks) mark(marks->dq_begin);
+  st = hip_status(bf ? dfa::launch_bwd_dq_bf16(a, hd, a.n_qtiles * BHq, s)
+                     : dfa::launch_bwd_dq_f32(a, hd, a.n_qtiles * BHq, s));
   if (st != DFA_OK) return st;
-  return hip_status(dfa::launch_bwd_dkdv_f32(a, hd, a.n_kvtiles * BHkv, s));
+  if (marks) mark(marks->dkdv_begin);
+  st = hip_status(bf ? dfa::launch_bwd_dkdv_bf16(a, hd, a.n_kvtiles * BHkv, s)
+                     : dfa::launch_bwd_dkdv_f32(a, hd, a.n_kvtiles * BHkv, s));
+  if (st != DFA_OK) return st;
+  if (marks) mark(marks->end);
+  return mark_ok ? DFA_OK : DFA_E_HIP;
 }

@@ -1,7 +1,8 @@
 """Shared helpers of the GPU parity tests: inputs, oracle calls and the
 tolerances.
 
-Tolerances (the benchmark spec's, with one derived reading for bf16 gradients):
+Tolerances (the stated accuracy targets, with one derived reading for bf16
+gradients):
 * fp32 path: |dO|, |dLSE| <= 1e-4; gradients max |dg| <= 1e-4 rms(g).
 * bf16 path: O max |dO| <= 2e-2 and mean <= 2e-3; LSE max <= 1e-3.
 * bf16 gradients: mean |dg| <= 2e-3 rms(g) as stated, and elementwise
