@@ -1,0 +1,98 @@
+"""GPU parity at the full workload sizes, on sampled outputs the fp64 oracle
+computes one by one: output rows and LSE of sampled query rows (random,
+first, last, chunk edges), dQ of those rows, and dK/dV of the last key rows
+(whose query rows the oracle can afford).  Heads are sampled as whole
+grouped-query groups so the oracle sees a consistent sub-problem.  The launch
+configuration is the benchmark's (fused forward, the same block lists)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import schedule_ref as sr
+from tests.parity_util import bhnd, check_grad, check_out, rows_of, to_np
+
+pytestmark = pytest.mark.gpu
+
+# name: (N, Hq, Hkv, kind, P, seed, qkv_scaled, rank, heads_sampled)
+WORKLOADS = {
+    "llama7b-n32k-balanced-p8": (32768, 32, 32, sr.BALANCED, 8, 1003, True, None, [0, 17]),
+    "llama7b-n131k-striped-p16-rank0": (131072, 32, 32, sr.STRIPED, 16, 1004, False, 0, [5]),
+    "gqa-32-8-n256k-balanced-p32": (262144, 32, 8, sr.BALANCED, 32, 1005, False, None, [1]),
+}
+
+
+@pytest.fixture(scope="module")
+def dfa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import long_context_sequence_dfa_amd as m
+    from long_context_sequence_dfa_amd import binding
+    binding.lib()
+    return m
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_sampled_parity(dfa, name):
+    from long_context_sequence_dfa_amd import inputs
+    N, Hq, Hkv, kind, P, seed, scaled, rank, kv_heads = WORKLOADS[name]
+    D, group = 128, Hq // Hkv
+    print(f"case: {name} generating inputs", flush=True)
+    qs = 1 / math.sqrt(D) if scaled else None
+    q, k, v, do = inputs.workload_tensors(seed, 1, N, Hq, Hkv, D, "bf16", qs, with_do=True)
+    dev = torch.device("cuda:0")
+    tq, tk, tv, tdo = (inputs.to_torch(x, "bf16", dev) for x in (q, k, v, do))
+    blocks = dfa.dfa_schedule_build(kind, N, P)
+    if rank is not None:
+        blocks = blocks[blocks[:, 0] == rank]
+    print(f"case: {name} forward + backward on the GPU ({len(blocks)} blocks)", flush=True)
+    o, lse = dfa.dfa_attn_fwd(tq, tk, tv, blocks)
+    dq, dk, dv = dfa.dfa_attn_bwd(tq, tk, tv, o, tdo, lse, blocks)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(dq.float()).all()
+    assert torch.isfinite(dk.float()).all() and torch.isfinite(dv.float()).all()
+
+    rows_all = rows_of(blocks)
+    rng = np.random.default_rng(seed)
+    chunk = N // (2 * P) if kind == sr.BALANCED else N // P
+    edges = [x for c in range(1, N // chunk) for x in (c * chunk - 1, c * chunk)]
+    cand = np.concatenate([rng.choice(rows_all, 40, replace=False), rows_all[:4], rows_all[-4:],
+                           np.array(edges[:8] + edges[-8:], dtype=np.int64)])
+    rows = np.intersect1d(np.unique(cand), rows_all)
+    scale = 1 / math.sqrt(D)
+    for hk in kv_heads:
+        heads = list(range(hk * group, (hk + 1) * group))
+        print(f"case: {name} oracle, kv head {hk}, {rows.size} rows", flush=True)
+        qh, doh = q[:, :, heads], do[:, :, heads]
+        kh, vh = k[:, :, [hk]], v[:, :, [hk]]
+        ro, rl = oracle.attn_rows(qh, kh, vh, scale, rows=rows)
+        go = bhnd(to_np(o[:, rows][:, :, heads]))
+        gl = to_np(lse[:, heads][:, :, rows])
+        check_out(go, ro, gl, rl, "bf16", f"{name} O")
+        lse_r, dd_r, rdq, aa, adq = oracle.grad_rows(qh, kh, vh, doh, scale, rows=rows, with_abs=True)
+        gq = bhnd(to_np(dq[:, rows][:, :, heads]))
+        # the rms of a sampled gradient set stands in for the tensor's
+        check_grad(gq, rdq, adq, "bf16", f"{name} dQ", check_mean=False)
+        # last key rows: their query rows are the tail of the row set
+        tail_rows = rows_all[rows_all >= N - 96]
+        keys = np.arange(N - 64, N)
+        l2, d2, _, a2, _ = oracle.grad_rows(qh, kh, vh, doh, scale, rows=tail_rows, with_abs=True)
+        rdk, rdv, adk, adv = oracle.grad_cols(qh, kh, vh, doh, scale, tail_rows, l2, d2, keys=keys,
+                                              aa=a2)
+        gk = bhnd(to_np(dk[:, keys][:, :, [hk]]))
+        gv = bhnd(to_np(dv[:, keys][:, :, [hk]]))
+        check_grad(gk, rdk, adk, "bf16", f"{name} dK", check_mean=False)
+        check_grad(gv, rdv, adv, "bf16", f"{name} dV", check_mean=False)
+    # whole-tensor invariants, valid at any size: softmax is shift invariant in
+    # k (sum_j dK_j = 0); sum_j dV_j = sum of dO over the rows and group heads
+    dkf = dk.double()
+    imb = dkf.sum(dim=1).abs()
+    assert torch.all(imb <= 2.0 ** -5 * dkf.abs().sum(dim=1) + 1e-3), f"{name} sum dK"
+    dof = tdo.double()[:, torch.as_tensor(rows_all, device=dev)]
+    want = dof.sum(dim=1).reshape(1, Hkv, group, D).sum(dim=2)
+    got = dv.double().sum(dim=1)
+    assert torch.all((got - want).abs() <= 2.0 ** -5 * dv.double().abs().sum(dim=1) + 1e-3), \
+        f"{name} sum dV"
+    print(f"case: {name} done", flush=True)
