@@ -39,6 +39,25 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Read of a schedule table entry that stays constant for the whole launch:
+// through the constant address space the compiler may use scalar loads and
+// keep everything derived from the entry in scalar registers.
+template <class T>
+__device__ __forceinline__ T ld_table(const T *p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return *(const __attribute__((address_space(4))) T *)(p);
+#else
+  return *p;  // host pass only; never executed
+#endif
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes
+// land at lds + 16 l (the LDS address must be uniform across the wave).
+__device__ __forceinline__ void load_lds16(const void *g, void *lds) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds(g, (lds_void *)(lds), 16, 0, 0);
+}
+
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
 

@@ -133,6 +133,14 @@ def test_calls_reject_bad_arguments_before_launch(bd):
                           fake, fake, fake, nul, 0, nul) == bd.DFA_E_WORKSPACE
     assert L.dfa_attn_bwd(ctypes.byref(d), arr, len(blocks), fake, fake, fake, fake, nul, fake,
                           fake, fake, fake, nul, 0, nul) == bd.DFA_E_NULL
+    # bf16 backward: 64 query rows of a piece must span less than 2^31 bytes
+    wide = desc(bd)
+    wide.q_strides[:] = [1 << 26, 1 << 24, 128]
+    assert L.dfa_attn_bwd(ctypes.byref(wide), arr, len(blocks), fake, fake, fake, fake, fake, fake,
+                          fake, fake, fake, nul, 0, nul) == bd.DFA_E_UNSUPPORTED
+    wide.q_strides[:] = [1 << 26, (1 << 24) - 8, 128]
+    assert L.dfa_attn_bwd(ctypes.byref(wide), arr, len(blocks), fake, fake, fake, fake, fake, fake,
+                          fake, fake, fake, nul, 0, nul) == bd.DFA_E_WORKSPACE
     blk = bd.DfaBlock(*[int(x) for x in blocks[0]])
     assert L.dfa_attn_block_fwd(ctypes.byref(desc(bd, head_dim=32)), ctypes.byref(blk), fake, fake,
                                 fake, fake, fake, nul) == bd.DFA_E_UNSUPPORTED
