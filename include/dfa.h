@@ -229,9 +229,9 @@ dfa_status dfa_attn_fwd(const dfa_attn_desc *d, const dfa_block *blocks, int64_t
  *   dq, dk, dv  : device, dtype, strides of q, k, v.  Overwritten; rows no
  *                 block touches are written as 0.  For grouped-query
  *                 attention dk and dv sum over the query heads of a group.
- * bf16 only: 64 consecutive rows of one query piece must span less than
- * 2^31 bytes in q and in d_o (64 * 2 * token stride * piece stride), else
- * DFA_E_UNSUPPORTED.
+ * bf16 only: 64 consecutive rows of one piece must span less than 2^31
+ * bytes in each of q, k, v and d_o (64 * 2 * token stride * piece stride),
+ * else DFA_E_UNSUPPORTED.
  */
 dfa_status dfa_attn_bwd(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n_blocks,
                         const void *q, const void *k, const void *v, const void *o,

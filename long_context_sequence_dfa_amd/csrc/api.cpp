@@ -630,8 +630,9 @@ extern "C" dfa_status dfa_attn_bwd_ex(const dfa_attn_desc *d, const dfa_block *b
   st = check_blocks(d, blocks, n_blocks);
   if (st != DFA_OK) return st;
   if (d->dtype == DFA_BF16) {
-    // the key-major kernels address 64 streamed query rows with 32-bit offsets
-    const int64_t row_bytes = 2 * std::max(d->q_strides[1], d->o_strides[1]);
+    // the gradient kernels address 64 streamed rows with 32-bit offsets
+    const int64_t row_bytes = 2 * std::max(std::max(d->q_strides[1], d->o_strides[1]),
+                                           std::max(d->k_strides[1], d->v_strides[1]));
     for (int64_t i = 0; i < n_blocks; ++i)
       if (row_bytes * blocks[i].stride >= (int64_t{1} << 31) / 64) return DFA_E_UNSUPPORTED;
   }

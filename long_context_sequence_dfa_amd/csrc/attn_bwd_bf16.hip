@@ -28,20 +28,102 @@ constexpr int NT = 256;
 
 __device__ __forceinline__ int kperm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+// Streamed operand tiles of 64 rows: pitch HD*2 + 32 bytes, logical 16-byte
+// chunk c of row r stored at chunk c ^ bit3(r).  Both the b128 reads of 16
+// rows (MFMA operands in kperm row order) and the transposing reads of 4 rows
+// x 32 bytes then hit distinct banks, and every operand address stays affine
+// in the loop indices.
+template <int HD>
+struct Tile64 {
+  static constexpr int ROWS = 64;
+  static constexpr int RB = HD * 2 + 32;       // row pitch in bytes
+  static constexpr int TB = ROWS * RB;         // tile bytes
+  static constexpr int LPR = HD * 2 / 16;      // data lanes per row in a direct load
+  static constexpr int LPRP = RB / 16;         // lanes per row including the pad
+  static constexpr int RPI = 64 / LPRP;        // rows per direct-load instruction
+  static constexpr int NI = (ROWS + RPI - 1) / RPI;  // instructions per tile
+  static constexpr int MW = (NI + 3) / 4;      // instructions per wave (4 waves)
+
+  // b128 operand read of row kperm(c32), chunk pair (2ks + g): offset + 32 ks
+  __device__ static int a_off(int lane) {
+    const int g = lane >> 5, c32 = lane & 31;
+    return kperm(c32) * RB + 16 * (g ^ ((c32 >> 2) & 1));
+  }
+  // transposing read: rows 16u + 8g + (lane&15)/4 (+4 for the upper half),
+  // 4 bf16 columns at 16((lane>>4)&1) + 4(lane&3) (+32 per column block)
+  __device__ static int t_off(int lane) {
+    const int g = lane >> 5;
+    return (8 * g + (lane & 15) / 4) * RB + 16 * ((2 * ((lane >> 4) & 1) + (lane & 3) / 2) ^ g) +
+           8 * (lane & 1);
+  }
+};
+
+// Direct HBM -> LDS loads of two 64-row tiles (same row count, separate row
+// strides) into the swizzled layout of Tile64.  A direct load writes 64 lanes
+// x 16 contiguous bytes, so LPRP lanes cover one padded row (pad lanes re-write
+// the row's first chunk into the pad).  Wave w issues instructions w, w + 4,
+// ...; each lane's row and chunk are fixed, so its byte offsets are computed
+// once (32-bit: the host guarantees 64 rows span less than 2^31 bytes).  Rows
+// past the piece re-read its last row; the caller's mask drops them.
+template <int HD>
+struct PairLoader {
+  using T = Tile64<HD>;
+  int wv, l_row, l_p;
+  int64_t rsa, rsb;
+  unsigned oa[T::MW], ob[T::MW];
+
+  __device__ int lrow(int m) const { return (wv + 4 * m) * T::RPI + l_row; }
+  __device__ int lchunk(int r) const { return l_p < T::LPR ? (l_p ^ ((r >> 3) & 1)) : 0; }
+  __device__ bool lon(int m) const { return wv + 4 * m < T::NI && l_row < T::RPI && lrow(m) < T::ROWS; }
+
+  __device__ PairLoader(int wave, int lane, int64_t rs_a, int64_t rs_b)
+      : wv(wave), l_row(lane / T::LPRP), l_p(lane % T::LPRP), rsa(rs_a), rsb(rs_b) {
+#pragma unroll
+    for (int m = 0; m < T::MW; ++m) {
+      const int r = lrow(m);
+      oa[m] = static_cast<unsigned>(r * rsa) + 16 * lchunk(r);
+      ob[m] = static_cast<unsigned>(r * rsb) + 16 * lchunk(r);
+    }
+  }
+
+  // ga/gb: first row of the tile; rows: rows left in the piece from there
+  __device__ void load(const char *ga, const char *gb, char *la, char *lb, int64_t rows) const {
+    if (rows >= T::ROWS) {
+#pragma unroll
+      for (int m = 0; m < T::MW; ++m)
+        if (wv + 4 * m < T::NI && lon(m)) {
+          const int r0 = (wv + 4 * m) * T::RPI;
+          load_lds16(ga + oa[m], la + r0 * T::RB);
+          load_lds16(gb + ob[m], lb + r0 * T::RB);
+        }
+    } else {
+      const int last = static_cast<int>(rows - 1);
+#pragma unroll
+      for (int m = 0; m < T::MW; ++m)
+        if (wv + 4 * m < T::NI && lon(m)) {
+          const int r0 = (wv + 4 * m) * T::RPI;
+          const int r = lrow(m), rr = r < last ? r : last;
+          load_lds16(ga + rr * rsa + 16 * lchunk(r), la + r0 * T::RB);
+          load_lds16(gb + rr * rsb + 16 * lchunk(r), lb + r0 * T::RB);
+        }
+    }
+  }
+};
+
 // ============================ dQ (query-major) ============================
 constexpr int DQ_BQ = kFwdTileQ;  // 128
 constexpr int DQ_BK = 64;
 
 template <int HD>
 __global__ __launch_bounds__(NT, 2) void dq_bf16_kernel(BwdArgs a) {
-  constexpr int PITCH = HD * 2 + 32;  // K tile: transposing reads of 4 rows conflict-free
-  constexpr int VPITCH = HD * 2 + 16; // V tile: b128 reads of 16 rows conflict-free
-  constexpr int TILEB = DQ_BK * PITCH;
-  constexpr int BUFB = TILEB + DQ_BK * VPITCH;
-  constexpr int KS = HD / 16, DT = HD / 32, CH = HD / 8, RPP = NT / CH, NP = DQ_BK / RPP;
+  using TL = Tile64<HD>;
+  static_assert(TL::ROWS == DQ_BK, "key tiles are 64 rows");
+  constexpr int RB = TL::RB, TB = TL::TB, BUFB = 2 * TB;  // K, V
+  constexpr int KS = HD / 16, DT = HD / 32;
   __shared__ __attribute__((aligned(16))) char smem[2 * BUFB];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, c32 = lane & 31;
   const Geom &G = a.g;
   const float c = G.scale_log2;
@@ -57,7 +139,6 @@ __global__ __launch_bounds__(NT, 2) void dq_bf16_kernel(BwdArgs a) {
 
   const char *kb = static_cast<const char *>(a.k) + 2 * (b * G.ks[0] + hk * G.ks[2]);
   const char *vb = static_cast<const char *>(a.v) + 2 * (b * G.vs[0] + hk * G.vs[2]);
-  const int64_t krs = 2 * G.ks[1] * seg.stride, vrs = 2 * G.vs[1] * seg.stride;
 
   // rows past the piece read its last row; they are never stored
   bf16x8 qf[KS], df[KS];
@@ -100,35 +181,21 @@ __global__ __launch_bounds__(NT, 2) void dq_bf16_kernel(BwdArgs a) {
     if (cw.ntiles > 0) break;
     ++k;
   }
-  const int lrow = tid / CH, lch = tid % CH;
-  u32x4 kr[NP], vr[NP];
-  // rows past the key piece re-read its last row; the mask zeroes them
-  auto gload = [&](const Walk &w, int64_t t) {
-    const char *kp = kb + 2 * w.kv_start * G.ks[1] + lch * 16;
-    const char *vp = vb + 2 * w.kv_start * G.vs[1] + lch * 16;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      int64_t j = t * DQ_BK + lrow + p * RPP;
-      j = j < w.len_kv ? j : w.len_kv - 1;
-      kr[p] = ld16(kp + j * krs);
-      vr[p] = ld16(vp + j * vrs);
-    }
-  };
-  auto lstore = [&](int buf) {
-    char *kt = smem + buf * BUFB;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      st16(kt + (lrow + p * RPP) * PITCH + lch * 16, kr[p]);
-      st16(kt + TILEB + (lrow + p * RPP) * VPITCH + lch * 16, vr[p]);
-    }
+  // K and V rows go straight into LDS
+  const PairLoader<HD> ld(wave, lane, 2 * G.ks[1] * seg.stride, 2 * G.vs[1] * seg.stride);
+  auto gload = [&](const Walk &w, int64_t t, int buf) {
+    char *base = smem + buf * BUFB;
+    const int64_t jt = t * DQ_BK;
+    const int64_t p0 = w.kv_start + jt * seg.stride;
+    ld.load(kb + 2 * p0 * G.ks[1], vb + 2 * p0 * G.vs[1], base, base + TB, w.len_kv - jt);
   };
   int64_t t = 0;
   int cur = 0;
-  if (k < nblk) {
-    gload(cw, 0);
-    lstore(0);
-  }
+  if (k < nblk) gload(cw, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  const int a_off = TL::a_off(lane);
+  const int t_off = TL::t_off(lane);
   while (k < nblk) {
     int kn = k;
     int64_t tn = t + 1;
@@ -142,62 +209,53 @@ __global__ __launch_bounds__(NT, 2) void dq_bf16_kernel(BwdArgs a) {
         ++kn;
       }
     }
-    const bool have_next = kn < nblk;
-    if (have_next) gload(nw, tn);
+    if (kn < nblk) gload(nw, tn, cur ^ 1);
 
     const int64_t j0 = t * DQ_BK;
     if (j0 <= i0w + 31 + cw.diag) {
       const char *kt = smem + cur * BUFB;
-      const char *vt = kt + TILEB;
-      f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
-      const int ro = kperm(c32) * PITCH + g * 16;
-      const int vo = kperm(c32) * VPITCH + g * 16;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 k0 = __builtin_bit_cast(bf16x8, ld16(kt + ro + ks * 32));
-        const bf16x8 k1 = __builtin_bit_cast(bf16x8, ld16(kt + ro + 32 * PITCH + ks * 32));
-        const bf16x8 v0 = __builtin_bit_cast(bf16x8, ld16(vt + vo + ks * 32));
-        const bf16x8 v1 = __builtin_bit_cast(bf16x8, ld16(vt + vo + 32 * VPITCH + ks * 32));
-        s0 = mfma32(k0, qf[ks], s0);
-        s1 = mfma32(k1, qf[ks], s1);
-        p0 = mfma32(v0, df[ks], p0);
-        p1 = mfma32(v1, df[ks], p1);
-      }
-      if ((j0 + DQ_BK - 1 > i0w + cw.diag) || (j0 + DQ_BK > cw.len_kv)) {
-        // local key j0 + jj is visible iff jj <= lim (32-bit)
+      const char *vt = kt + TB;
+      const bool need_mask = (j0 + DQ_BK - 1 > i0w + cw.diag) || (j0 + DQ_BK > cw.len_kv);
+      int x = 0;
+      if (need_mask) {
+        // element i of half kh is local key jj = 32kh + 16(i/8) + 8g + i%8,
+        // visible iff jj <= lim; x = 8g - lim
         const int64_t lim64 = row + cw.diag - j0, len64 = cw.len_kv - 1 - j0;
         const int64_t m64 = lim64 < len64 ? lim64 : len64;
-        const int lim = static_cast<int>(m64 < -1 ? -1 : m64);
+        x = 8 * g - static_cast<int>(m64 < -1 ? -1 : (m64 > DQ_BK ? DQ_BK : m64));
+      }
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {  // two halves of 32 keys
+        f32x16 sv = f32x16{}, pv = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int o = a_off + 32 * kh * RB + ks * 32;
+          sv = mfma32(__builtin_bit_cast(bf16x8, ld16(kt + o)), qf[ks], sv);
+          pv = mfma32(__builtin_bit_cast(bf16x8, ld16(vt + o)), df[ks], pv);
+        }
+        if (need_mask) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (x + 32 * kh + 16 * (i / 8) + (i % 8) > 0) sv[i] = -INFINITY;
+        }
+        bf16x8 dsb[2];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int jj = 16 * (i / 8) + 8 * g + (i % 8);
-          if (jj > lim) s0[i] = -INFINITY;
-          if (jj + 32 > lim) s1[i] = -INFINITY;
+          const float pa = fast_exp2(__builtin_fmaf(sv[i], c, -lse2));
+          dsb[i / 8][i % 8] = static_cast<__bf16>(pa * (pv[i] - dd));
         }
-      }
-      bf16x8 dsb[4];
+        // dQ^T += K^T dS^T: A = K^T (d x 16 keys) read transposed from the K tile
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pa = fast_exp2(__builtin_fmaf(s0[i], c, -lse2));
-        const float pc = fast_exp2(__builtin_fmaf(s1[i], c, -lse2));
-        dsb[i / 8][i % 8] = static_cast<__bf16>(pa * (p0[i] - dd));
-        dsb[2 + i / 8][i % 8] = static_cast<__bf16>(pc * (p1[i] - dd));
-      }
-      // dQ^T += K^T dS^T: A = K^T (d x 16 keys) read transposed from the K tile
-      const int krow = 8 * g + (lane & 15) / 4;
-      const int kcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        for (int u = 0; u < 2; ++u) {
+          const int o = t_off + 16 * (2 * kh + u) * RB;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const char *kp = kt + (16 * kk + krow) * PITCH + kcol * 2;  // kt: current K tile
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const bf16x4 lo = lds_read_tr(kp + dt * 64);
-          const bf16x4 hi = lds_read_tr(kp + 4 * PITCH + dt * 64);
-          acc[dt] = mfma32(cat8(lo, hi), dsb[kk], acc[dt]);
+          for (int dt = 0; dt < DT; ++dt)
+            acc[dt] = mfma32(cat8(lds_read_tr(kt + o + 64 * dt), lds_read_tr(kt + o + 4 * RB + 64 * dt)),
+                             dsb[u], acc[dt]);
         }
       }
     }
-    if (have_next) lstore(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
     __syncthreads();
     cur ^= 1;
     k = kn;
@@ -229,18 +287,12 @@ constexpr int KV_DV = 1, KV_DK = 2;
 
 template <int HD, int MODE>
 __global__ __launch_bounds__(NT, 2) void dkdv_bf16_kernel(BwdArgs a) {
-  // Streamed Q/dO tiles: pitch HD*2 + 32 and logical 16-byte chunk c of row r
-  // stored at chunk c ^ bit3(r).  Both the b128 row reads of 16 rows and the
-  // transposing reads of 4 rows x 32 bytes then hit distinct banks, and every
-  // operand address stays affine in the loop indices.
-  constexpr int RB = HD * 2 + 32;
-  constexpr int TB = KV_BQ * RB;
+  using TL = Tile64<HD>;
+  static_assert(TL::ROWS == KV_BQ, "query tiles are 64 rows");
+  constexpr int RB = TL::RB;
+  constexpr int TB = TL::TB;
   constexpr int BUFB = 2 * TB + 2 * KV_BQ * 4;  // Q, dO, LSE*log2(e), D
   constexpr int KS = HD / 16, DT = HD / 32;
-  constexpr int LPR = HD * 2 / 16;           // data lanes per row in a direct load
-  constexpr int LPRP = RB / 16;              // lanes per row including the pad
-  constexpr int RPI = 64 / LPRP;             // rows per direct load instruction
-  constexpr int NI = (KV_BQ + RPI - 1) / RPI;   // direct loads per tile and tensor
   constexpr bool DK = MODE == KV_DK;
   __shared__ __attribute__((aligned(16))) char smem[2 * BUFB];
 
@@ -310,30 +362,10 @@ __global__ __launch_bounds__(NT, 2) void dkdv_bf16_kernel(BwdArgs a) {
   advance_to_nonempty(gi, k, cw);
   int64_t t = cw.t0;
 
-  // bytes between consecutive rows of the piece (the host guarantees that 64
-  // rows span less than 2^31 bytes, so per-lane row offsets fit 32 bits)
-  const int64_t qrs = 2 * G.qs[1] * seg.stride, ors = 2 * G.os[1] * seg.stride;
   float lsr = 0.f, ddr = 0.f;
-  // Q and dO rows go straight from HBM into the LDS tile (no registers): a
-  // direct load writes 64 lanes x 16 contiguous bytes, so LPRP lanes cover one
-  // padded row (the pad lanes re-write the row's first chunk into the pad).
-  // Wave w issues loads w, w + 4, ...; each lane's row and chunk are fixed,
-  // so its byte offsets are computed once.  Rows past the query piece re-read
-  // its last row (ragged tiles only) and the mask drops them.  LSE and D of
-  // the 64 rows travel through two registers.
-  constexpr int MW = (NI + 3) / 4;  // loads per wave and tensor
-  const int wv = wave;
-  const int l_row = lane / LPRP, l_p = lane % LPRP;
-  auto lrow = [&](int m) { return (wv + 4 * m) * RPI + l_row; };
-  auto lchunk = [&](int r) { return l_p < LPR ? (l_p ^ ((r >> 3) & 1)) : 0; };
-  auto lon = [&](int m) { return wv + 4 * m < NI && l_row < RPI && lrow(m) < KV_BQ; };
-  unsigned qo_m[MW], oo_m[MW];
-#pragma unroll
-  for (int m = 0; m < MW; ++m) {
-    const int r = lrow(m);
-    qo_m[m] = static_cast<unsigned>(r * qrs) + 16 * lchunk(r);
-    oo_m[m] = static_cast<unsigned>(r * ors) + 16 * lchunk(r);
-  }
+  // Q and dO rows go straight into LDS; LSE and D of the 64 rows travel
+  // through two registers.
+  const PairLoader<HD> ld(wave, lane, 2 * G.qs[1] * seg.stride, 2 * G.os[1] * seg.stride);
   auto dload = [&](const Walk &w, int64_t tt, int buf) {
     char *base = smem + buf * BUFB;
     const int64_t i0 = tt * KV_BQ;
@@ -341,27 +373,7 @@ __global__ __launch_bounds__(NT, 2) void dkdv_bf16_kernel(BwdArgs a) {
                      2 * (b * G.qs[0] + (w.q_start + i0 * seg.stride) * G.qs[1] + w.h * G.qs[2]);
     const char *db = static_cast<const char *>(a.dout) +
                      2 * (b * G.os[0] + (w.q_start + i0 * seg.stride) * G.os[1] + w.h * G.os[2]);
-    if (i0 + KV_BQ <= w.len_q) {
-#pragma unroll
-      for (int m = 0; m < MW; ++m) {
-        if (wv + 4 * m < NI && lon(m)) {
-          const int r0 = (wv + 4 * m) * RPI;
-          load_lds16(qb + qo_m[m], base + r0 * RB);
-          load_lds16(db + oo_m[m], base + TB + r0 * RB);
-        }
-      }
-    } else {  // ragged last tile: rows past the piece re-read its last row
-      const int last = static_cast<int>(w.len_q - 1 - i0);
-#pragma unroll
-      for (int m = 0; m < MW; ++m) {
-        if (wv + 4 * m < NI && lon(m)) {
-          const int r0 = (wv + 4 * m) * RPI;
-          const int r = lrow(m), rr = r < last ? r : last;
-          load_lds16(qb + rr * qrs + 16 * lchunk(r), base + r0 * RB);
-          load_lds16(db + rr * ors + 16 * lchunk(r), base + TB + r0 * RB);
-        }
-      }
-    }
+    ld.load(qb, db, base, base + TB, w.len_q - i0);
     if (tid < KV_BQ) {
       int64_t i = i0 + tid;
       i = i < w.len_q ? i : w.len_q - 1;
@@ -388,9 +400,8 @@ __global__ __launch_bounds__(NT, 2) void dkdv_bf16_kernel(BwdArgs a) {
 
   // per-lane operand offsets (independent of the tile); loop indices only
   // add compile-time constants to them
-  const int a_off = kperm(c32) * RB + 16 * (g ^ ((c32 >> 2) & 1));
-  const int t_off = (8 * g + (lane & 15) / 4) * RB +
-                    16 * ((2 * ((lane >> 4) & 1) + (lane & 3) / 2) ^ g) + 8 * (lane & 1);
+  const int a_off = TL::a_off(lane);
+  const int t_off = TL::t_off(lane);
   while (gi < ngrp) {
     int gn = gi, kn = k;
     int64_t tn = t + 1;
