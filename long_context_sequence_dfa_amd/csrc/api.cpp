@@ -260,6 +260,7 @@ dfa::Geom make_geom(const dfa_attn_desc *d) {
 }
 
 int fwd_tile(const dfa_attn_desc *d) { return d->dtype == DFA_BF16 ? dfa::kFwdTileQ : dfa::kF32TileQ; }
+int dq_tile(const dfa_attn_desc *d) { return d->dtype == DFA_BF16 ? dfa::kDqTileQ : dfa::kF32TileQ; }
 int kv_tile(const dfa_attn_desc *d) { return d->dtype == DFA_BF16 ? dfa::kBwdTileKV : dfa::kF32TileKV; }
 
 dfa_status hip_status(hipError_t e) { return e == hipSuccess ? DFA_OK : DFA_E_HIP; }
@@ -461,7 +462,7 @@ extern "C" dfa_status dfa_workspace_size(const dfa_attn_desc *d, const dfa_block
   } else if (op == DFA_OP_BWD) {
     QPlan qp;
     KvPlan kp;
-    st = plan_q(d, blocks, n_blocks, fwd_tile(d), qp);
+    st = plan_q(d, blocks, n_blocks, dq_tile(d), qp);
     if (st != DFA_OK) return st;
     st = plan_kv(d, blocks, n_blocks, kv_tile(d), kp);
     if (st != DFA_OK) return st;
@@ -638,7 +639,7 @@ extern "C" dfa_status dfa_attn_bwd_ex(const dfa_attn_desc *d, const dfa_block *b
   }
   QPlan qp;
   KvPlan kp;
-  st = plan_q(d, blocks, n_blocks, fwd_tile(d), qp);
+  st = plan_q(d, blocks, n_blocks, dq_tile(d), qp);
   if (st != DFA_OK) return st;
   st = plan_kv(d, blocks, n_blocks, kv_tile(d), kp);
   if (st != DFA_OK) return st;

@@ -111,7 +111,7 @@ struct PairLoader {
 };
 
 // ============================ dQ (query-major) ============================
-constexpr int DQ_BQ = kFwdTileQ;  // 128
+constexpr int DQ_BQ = kDqTileQ;  // 128
 constexpr int DQ_BK = 64;
 
 template <int HD>

@@ -32,27 +32,31 @@
 //    than 2^8 (exact: every probability is taken against the same reference
 //    max as its row sum, and stays below 2^8).
 // Score arithmetic runs in the log2 domain: x = s * scale * log2(e).
-#include "device_util.h"
 #include "dfa_internal.h"
+#include "stream_lds.h"
 
 namespace dfa {
 namespace {
 
-constexpr int BQ = kFwdTileQ;  // 128 query rows per workgroup
-constexpr int BK = 64;         // keys per tile
-constexpr int NT = 256;        // threads per workgroup
-
-// Row order of key tiles inside the S^T MFMA: swaps bits 2 and 3 of the
-// row index (see the header comment).
-__device__ __forceinline__ int kperm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+constexpr int NW = kFwdWaves;  // waves per workgroup
+constexpr int NT = 64 * NW;    // threads per workgroup
+constexpr int BQ = kFwdTileQ;  // query rows per workgroup (32 per wave)
+constexpr int BK = 64;         // keys per streamed tile
+constexpr int NS = kFwdStages; // K/V tiles resident in LDS (NS - 1 in flight)
+static_assert(BQ == 32 * NW, "one 32-query column block per wave");
 
 struct BlockWalk {
   int64_t kv_start, len_kv, diag, ntiles;
 };
 
+template <bool TABLE>
 __device__ __forceinline__ BlockWalk block_walk(const FwdArgs &a, const QSeg &seg, int k,
                                                 int64_t iend) {
-  KvRef r = a.segs ? a.kv[seg.blk_begin + k] : a.kv0;
+  KvRef r;
+  if constexpr (TABLE)
+    r = ld_table(a.kv + seg.blk_begin + k);
+  else
+    r = a.kv0;
   BlockWalk w;
   w.kv_start = r.kv_start;
   w.len_kv = r.len_kv;
@@ -64,21 +68,21 @@ __device__ __forceinline__ BlockWalk block_walk(const FwdArgs &a, const QSeg &se
   return w;
 }
 
-template <int HD, int OUT>
-__global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdArgs a) {
-  constexpr int KP = HD * 2 + 16;   // K tile pitch: b128 reads of 16 rows are conflict-free
-  constexpr int VP = HD * 2 + 32;   // V tile pitch: transposing reads of 4 rows are conflict-free
-  constexpr int KB = BK * KP;
-  constexpr int BUF = KB + BK * VP;
+// TABLE: the query piece and its blocks come from the work tables (fused and
+// stepwise walks); otherwise from seg0/kv0 (one block).
+template <int HD, int OUT, bool TABLE>
+__global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
+  using TL = Tile64<HD>;
+  static_assert(TL::ROWS == BK, "key tiles are 64 rows");
+  constexpr int RB = TL::RB, TB = TL::TB;
+  constexpr int STAGE = 2 * TB;     // K tile, V tile
   constexpr int KS = HD / 16;       // MFMA k-steps over head_dim
   constexpr int DT = HD / 32;       // 32-row output tiles over head_dim
-  constexpr int CH = HD / 8;        // 16-byte chunks per row
-  constexpr int RPP = NT / CH;      // rows per load pass
-  constexpr int NP = BK / RPP;      // load passes per tile
   constexpr float TAU = 8.f;        // lazy rescale threshold (log2 units)
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+  __shared__ __attribute__((aligned(16))) char smem[NS * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, c32 = lane & 31;
   const Geom &G = a.g;
   const int BH = G.batch * G.hq;
@@ -89,9 +93,9 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdArgs a) {
 
   QSeg seg;
   int64_t qt;
-  if (a.segs) {
-    const Tile t = a.tiles[ti];
-    seg = a.segs[t.seg];
+  if constexpr (TABLE) {
+    const Tile t = ld_table(a.tiles + ti);
+    seg = ld_table(a.segs + t.seg);
     qt = t.tile;
   } else {
     seg = a.seg0;
@@ -105,7 +109,6 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdArgs a) {
   const char *qb = static_cast<const char *>(a.q) + 2 * (b * G.qs[0] + h * G.qs[2]);
   const char *kb = static_cast<const char *>(a.k) + 2 * (b * G.ks[0] + hk * G.ks[2]);
   const char *vb = static_cast<const char *>(a.v) + 2 * (b * G.vs[0] + hk * G.vs[2]);
-  const int64_t krs = 2 * G.ks[1] * seg.stride, vrs = 2 * G.vs[1] * seg.stride;  // bytes per row
 
   // Q^T operand (B of S^T = K Q^T): lane holds Q[row][16ks + 8g .. +8].
   // Rows past the piece read its last row (their outputs are never stored).
@@ -123,90 +126,82 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdArgs a) {
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // ---- tile walk state ----
+  // ---- tile sequence: (block k, tile t) over the blocks with visible keys ----
+  const int nblk = TABLE ? seg.blk_count : 1;
+  auto first = [&](int &k_, BlockWalk &w_) {
+    while (k_ < nblk) {
+      w_ = block_walk<TABLE>(a, seg, k_, iend);
+      if (w_.ntiles > 0) return;
+      ++k_;
+    }
+  };
+  auto next = [&](int &k_, int64_t &t_, BlockWalk &w_) {
+    if (++t_ < w_.ntiles) return;
+    t_ = 0;
+    ++k_;
+    first(k_, w_);
+  };
   int k = 0;
-  BlockWalk cw{0, 0, 0, 0};
-  const int nblk = a.segs ? seg.blk_count : 1;
-  while (k < nblk) {
-    cw = block_walk(a, seg, k, iend);
-    if (cw.ntiles > 0) break;
-    ++k;
-  }
-
-  const int lrow = tid / CH, lch = tid % CH;
-  u32x4 kr[NP], vr[NP];
-  // rows past the block's key piece re-read its last row; the mask zeroes them
-  auto gload = [&](const BlockWalk &w, int64_t t) {
-    const char *kp = kb + 2 * w.kv_start * G.ks[1] + lch * 16;
-    const char *vp = vb + 2 * w.kv_start * G.vs[1] + lch * 16;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      int64_t j = t * BK + lrow + p * RPP;
-      j = j < w.len_kv ? j : w.len_kv - 1;
-      kr[p] = ld16(kp + j * krs);
-      vr[p] = ld16(vp + j * vrs);
-    }
-  };
-  auto lstore = [&](int buf) {
-    char *kt = smem + buf * BUF;
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      st16(kt + (lrow + p * RPP) * KP + lch * 16, kr[p]);
-      st16(kt + KB + (lrow + p * RPP) * VP + lch * 16, vr[p]);
-    }
-  };
-
   int64_t t = 0;
-  int cur = 0;
-  if (k < nblk) {
-    gload(cw, 0);
-    lstore(0);
-  }
-  __syncthreads();
+  BlockWalk cw{0, 0, 0, 0};
+  first(k, cw);
 
-  const int kr0 = kperm(c32) * KP + g * 16;
-  const int vrow = 8 * g + (lane & 15) / 4;
-  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const int voff = vrow * VP + vcol * 2;
+  // ---- K/V stream: NS LDS stages, the load cursor runs NS - 1 tiles ahead ----
+  const TileStream<HD, NW> ld(wave, lane, 2 * G.ks[1] * seg.stride, 2 * G.vs[1] * seg.stride);
+  const int per_tile = 2 * ld.count();
+  const unsigned lds0 = lds_addr(smem);
+  int kl = k;
+  int64_t tl = 0;
+  BlockWalk lw = cw;
+  int issued = 0;
+  auto issue = [&](int stage) {
+    const int64_t j0 = tl * BK;
+    const int64_t p0 = lw.kv_start + j0 * seg.stride;
+    ld.load(kb + 2 * p0 * G.ks[1], vb + 2 * p0 * G.vs[1], lds0 + stage * STAGE,
+            lds0 + stage * STAGE + TB, lw.len_kv - j0);
+    ++issued;
+    next(kl, tl, lw);
+  };
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (kl < nblk) issue(s);
+  // the Q fragments and the first tiles have landed; from here on the only
+  // vector-memory operations in flight are the tile loads counted above
+  vm_wait<0>();
+
+  const int a_off = TL::a_off(lane);
+  const int t_off = TL::t_off(lane);
+  int it = 0;
   while (k < nblk) {
-    // next (block, tile)
-    int kn = k;
-    int64_t tn = t + 1;
-    BlockWalk nw = cw;
-    if (tn >= cw.ntiles) {
-      tn = 0;
-      ++kn;
-      while (kn < nblk) {
-        nw = block_walk(a, seg, kn, iend);
-        if (nw.ntiles > 0) break;
-        ++kn;
-      }
-    }
-    const bool have_next = kn < nblk;
-    if (have_next) gload(nw, tn);
+    // this wave's loads of tile `it` have landed once at most the loads of
+    // the tiles issued after it are outstanding; the barrier then publishes
+    // every wave's part and frees the stage read in the previous iteration
+    vm_wait((issued - 1 - it) * per_tile);
+    __syncthreads();
+    if (kl < nblk) issue((it + NS - 1) % NS);
 
-    // ---- compute the current tile ----
     const int64_t j0 = t * BK;
     if (j0 <= i0w + 31 + cw.diag) {  // some row of this wave sees a key of the tile
-      const char *kt = smem + cur * BUF;
-      const char *vt = kt + KB;
+      const char *kt = smem + (it % NS) * STAGE;
+      const char *vt = kt + TB;
       f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s0 = mfma32(__builtin_bit_cast(bf16x8, ld16(kt + kr0 + ks * 32)), qf[ks], s0);
-        s1 = mfma32(__builtin_bit_cast(bf16x8, ld16(kt + kr0 + 32 * KP + ks * 32)), qf[ks], s1);
+        s0 = mfma32(__builtin_bit_cast(bf16x8, ld16(kt + a_off + ks * 32)), qf[ks], s0);
+        s1 = mfma32(__builtin_bit_cast(bf16x8, ld16(kt + a_off + 32 * RB + ks * 32)), qf[ks], s1);
       }
       // element i of s0 / s1 is key j0 + 32*(i/16) + 16*((i%16)/8) + 8g + i%8
       if ((j0 + BK - 1 > i0w + cw.diag) || (j0 + BK > cw.len_kv)) {
-        // 32-bit local offsets: key j0 + jj is visible iff jj <= lim
+        // key j0 + jj is visible iff jj <= lim; x = 8g - lim
         const int64_t lim64 = i0w + c32 + cw.diag - j0;
         const int64_t len64 = cw.len_kv - 1 - j0;
-        const int lim = static_cast<int>(lim64 < len64 ? (lim64 < -1 ? -1 : lim64) : (len64 < -1 ? -1 : len64));
+        const int64_t m64 = lim64 < len64 ? lim64 : len64;
+        const int x = 8 * g - static_cast<int>(m64 < -1 ? -1 : (m64 > BK ? BK : m64));
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int jj = 16 * (i / 8) + 8 * g + (i % 8);
-          if (jj > lim) s0[i] = -INFINITY;
-          if (jj + 32 > lim) s1[i] = -INFINITY;
+          const int kc = 16 * (i / 8) + (i % 8);
+          if (x + kc > 0) s0[i] = -INFINITY;
+          if (x + kc + 32 > 0) s1[i] = -INFINITY;
         }
       }
       float mx = fmaxf(s0[0], s1[0]);
@@ -238,25 +233,18 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdArgs a) {
         pb[2 + i / 8][i % 8] = static_cast<__bf16>(p1);
       }
       l_run += psum;
-      // O^T += V^T P^T: A = V^T rows (d) x 16 keys, read transposed from LDS
+      // O^T += V^T P^T: A = V^T (d x 16 keys) read transposed from the V tile
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const char *vp = vt + 16 * kk * VP + voff;
+        const int o = t_off + 16 * kk * RB;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const bf16x4 lo = lds_read_tr(vp + dt * 64);
-          const bf16x4 hi = lds_read_tr(vp + 4 * VP + dt * 64);
-          acc[dt] = mfma32(cat8(lo, hi), pb[kk], acc[dt]);
-        }
+        for (int dt = 0; dt < DT; ++dt)
+          acc[dt] = mfma32(cat8(lds_read_tr(vt + o + 64 * dt), lds_read_tr(vt + o + 4 * RB + 64 * dt)),
+                           pb[kk], acc[dt]);
       }
     }
-
-    if (have_next) lstore(cur ^ 1);
-    __syncthreads();
-    cur ^= 1;
-    k = kn;
-    t = tn;
-    cw = nw;
+    next(k, t, cw);
+    ++it;
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
@@ -301,17 +289,22 @@ __global__ __launch_bounds__(NT, 2) void fwd_bf16_kernel(FwdArgs a) {
 hipError_t launch_fwd_bf16(const FwdArgs &a, int hd, int64_t grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  dim3 gr(static_cast<unsigned>(grid)), bl(NT);
+  if (a.out_mode == 0 && !a.segs) return hipErrorInvalidValue;
+  const dim3 gr(static_cast<unsigned>(grid)), bl(NT);
   if (hd == 128) {
     if (a.out_mode == 0)
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, 0>), gr, bl, 0, s, a);
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, 0, true>), gr, bl, 0, s, a);
+    else if (a.segs)
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, 1, true>), gr, bl, 0, s, a);
     else
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, 1>), gr, bl, 0, s, a);
+      hipLaunchKernelGGL((fwd_bf16_kernel<128, 1, false>), gr, bl, 0, s, a);
   } else if (hd == 64) {
     if (a.out_mode == 0)
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, 0>), gr, bl, 0, s, a);
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, 0, true>), gr, bl, 0, s, a);
+    else if (a.segs)
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, 1, true>), gr, bl, 0, s, a);
     else
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, 1>), gr, bl, 0, s, a);
+      hipLaunchKernelGGL((fwd_bf16_kernel<64, 1, false>), gr, bl, 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -39,16 +39,55 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Read of a schedule table entry that stays constant for the whole launch:
-// through the constant address space the compiler may use scalar loads and
-// keep everything derived from the entry in scalar registers.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
+  const unsigned lo = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(x));
+  const unsigned hi = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(x >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Read of a work-table entry (wave-uniform address, constant for the whole
+// launch) with scalar loads (early-clobber outputs: the second load of a
+// pair still reads the base).  Written as inline assembly so that it stays a
+// scalar load even where the compiler cannot prove the memory unmodified: a
+// vector load here would share the vector-memory counter with the tile
+// streams, and waiting for it would also wait for every tile in flight.
+typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ void sload_words(uint64_t b, uint32_t (&w)[2]) {
+  u32x2 x;
+  asm("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(x) : "s"(b));
+  w[0] = x[0], w[1] = x[1];
+}
+__device__ __forceinline__ void sload_words(uint64_t b, uint32_t (&w)[6]) {
+  u32x4 x;
+  u32x2 y;
+  asm("s_load_dwordx4 %0, %2, 0x0\n\ts_load_dwordx2 %1, %2, 0x10\n\ts_waitcnt lgkmcnt(0)"
+      : "=&s"(x), "=&s"(y)
+      : "s"(b));
+  for (int i = 0; i < 4; ++i) w[i] = x[i];
+  w[4] = y[0], w[5] = y[1];
+}
+__device__ __forceinline__ void sload_words(uint64_t b, uint32_t (&w)[8]) {
+  u32x8_t x;
+  asm("s_load_dwordx8 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(x) : "s"(b));
+  for (int i = 0; i < 8; ++i) w[i] = x[i];
+}
+__device__ __forceinline__ void sload_words(uint64_t b, uint32_t (&w)[10]) {
+  u32x8_t x;
+  u32x2 y;
+  asm("s_load_dwordx8 %0, %2, 0x0\n\ts_load_dwordx2 %1, %2, 0x20\n\ts_waitcnt lgkmcnt(0)"
+      : "=&s"(x), "=&s"(y)
+      : "s"(b));
+  for (int i = 0; i < 8; ++i) w[i] = x[i];
+  w[8] = y[0], w[9] = y[1];
+}
 template <class T>
 __device__ __forceinline__ T ld_table(const T *p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  return *(const __attribute__((address_space(4))) T *)(p);
-#else
-  return *p;  // host pass only; never executed
-#endif
+  static_assert(sizeof(T) % 4 == 0, "table entries are whole dwords");
+  uint32_t w[sizeof(T) / 4];
+  sload_words(uniform_u64(reinterpret_cast<uint64_t>(p)), w);
+  T r;
+  __builtin_memcpy(&r, w, sizeof(T));
+  return r;
 }
 
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes

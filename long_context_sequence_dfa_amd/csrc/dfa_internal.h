@@ -85,7 +85,10 @@ struct MergeItem {
 };
 
 // Tile shapes (rows per work item).
-constexpr int kFwdTileQ = 128;   // bf16 forward / dq: query rows per workgroup
+constexpr int kFwdWaves = 8;                // bf16 forward: waves per workgroup
+constexpr int kFwdTileQ = 32 * kFwdWaves;   // bf16 forward: query rows per workgroup
+constexpr int kFwdStages = 4;               // bf16 forward: K/V tiles resident in LDS
+constexpr int kDqTileQ = 128;               // bf16 dq: query rows per workgroup
 constexpr int kBwdTileKV = 128;  // bf16 dk/dv: key rows per workgroup
 constexpr int kF32TileQ = 64;    // fp32 kernels: rows per workgroup
 constexpr int kF32TileKV = 64;
