@@ -359,7 +359,7 @@ struct StepLayout {
   size_t segs, kv, tiles, items, acc_o, acc_lse, part_o, part_lse, total;
 };
 struct BwdLayout {
-  size_t qsegs, qkv, qtiles, kvsegs, kvq, kvtiles, dd, total;
+  size_t qsegs, qkv, qtiles, kvsegs, kvq, kvtiles, dd, lse2, total;
 };
 
 template <class T>
@@ -402,7 +402,8 @@ BwdLayout bwd_layout(const dfa_attn_desc *d, const QPlan &qp, const KvPlan &kp) 
   L.kvq = L.kvsegs + vbytes(kp.segs);
   L.kvtiles = L.kvq + vbytes(kp.q);
   L.dd = L.kvtiles + vbytes(kp.tiles);
-  L.total = L.dd + align_up(rows * sizeof(float));
+  L.lse2 = L.dd + align_up(rows * sizeof(float));
+  L.total = L.lse2 + align_up(rows * sizeof(float));
   return L;
 }
 
@@ -681,6 +682,7 @@ extern "C" dfa_status dfa_attn_bwd_ex(const dfa_attn_desc *d, const dfa_block *b
   a.dout = d_o;
   a.lse = lse;
   a.dd = reinterpret_cast<float *>(ws + L.dd);
+  a.lse2 = reinterpret_cast<float *>(ws + L.lse2);
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;

@@ -16,111 +16,31 @@
 //    registers as MFMA operands), walks every block that reads its key piece
 //    and every query head of its group, and computes S = Q K^T, dP = dO V^T,
 //    dV^T += dO^T P and dK^T += Q^T dS.  Each lane owns one key column.
-// Q/dO (or K/V) tiles are double-buffered in LDS; transposed operands come
+// Both stream 64-row K/V (or Q/dO) tiles through NS LDS stages with direct
+// loads issued NS - 1 tiles ahead (stream_lds.h); transposed operands come
 // from ds_read_b64_tr_b16 on the row-major tiles.
-#include "device_util.h"
 #include "dfa_internal.h"
+#include "stream_lds.h"
 
 namespace dfa {
 namespace {
 
-constexpr int NT = 256;
-
-__device__ __forceinline__ int kperm(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
-
-// Streamed operand tiles of 64 rows: pitch HD*2 + 32 bytes, logical 16-byte
-// chunk c of row r stored at chunk c ^ bit3(r).  Both the b128 reads of 16
-// rows (MFMA operands in kperm row order) and the transposing reads of 4 rows
-// x 32 bytes then hit distinct banks, and every operand address stays affine
-// in the loop indices.
-template <int HD>
-struct Tile64 {
-  static constexpr int ROWS = 64;
-  static constexpr int RB = HD * 2 + 32;       // row pitch in bytes
-  static constexpr int TB = ROWS * RB;         // tile bytes
-  static constexpr int LPR = HD * 2 / 16;      // data lanes per row in a direct load
-  static constexpr int LPRP = RB / 16;         // lanes per row including the pad
-  static constexpr int RPI = 64 / LPRP;        // rows per direct-load instruction
-  static constexpr int NI = (ROWS + RPI - 1) / RPI;  // instructions per tile
-  static constexpr int MW = (NI + 3) / 4;      // instructions per wave (4 waves)
-
-  // b128 operand read of row kperm(c32), chunk pair (2ks + g): offset + 32 ks
-  __device__ static int a_off(int lane) {
-    const int g = lane >> 5, c32 = lane & 31;
-    return kperm(c32) * RB + 16 * (g ^ ((c32 >> 2) & 1));
-  }
-  // transposing read: rows 16u + 8g + (lane&15)/4 (+4 for the upper half),
-  // 4 bf16 columns at 16((lane>>4)&1) + 4(lane&3) (+32 per column block)
-  __device__ static int t_off(int lane) {
-    const int g = lane >> 5;
-    return (8 * g + (lane & 15) / 4) * RB + 16 * ((2 * ((lane >> 4) & 1) + (lane & 3) / 2) ^ g) +
-           8 * (lane & 1);
-  }
-};
-
-// Direct HBM -> LDS loads of two 64-row tiles (same row count, separate row
-// strides) into the swizzled layout of Tile64.  A direct load writes 64 lanes
-// x 16 contiguous bytes, so LPRP lanes cover one padded row (pad lanes re-write
-// the row's first chunk into the pad).  Wave w issues instructions w, w + 4,
-// ...; each lane's row and chunk are fixed, so its byte offsets are computed
-// once (32-bit: the host guarantees 64 rows span less than 2^31 bytes).  Rows
-// past the piece re-read its last row; the caller's mask drops them.
-template <int HD>
-struct PairLoader {
-  using T = Tile64<HD>;
-  int wv, l_row, l_p;
-  int64_t rsa, rsb;
-  unsigned oa[T::MW], ob[T::MW];
-
-  __device__ int lrow(int m) const { return (wv + 4 * m) * T::RPI + l_row; }
-  __device__ int lchunk(int r) const { return l_p < T::LPR ? (l_p ^ ((r >> 3) & 1)) : 0; }
-  __device__ bool lon(int m) const { return wv + 4 * m < T::NI && l_row < T::RPI && lrow(m) < T::ROWS; }
-
-  __device__ PairLoader(int wave, int lane, int64_t rs_a, int64_t rs_b)
-      : wv(wave), l_row(lane / T::LPRP), l_p(lane % T::LPRP), rsa(rs_a), rsb(rs_b) {
-#pragma unroll
-    for (int m = 0; m < T::MW; ++m) {
-      const int r = lrow(m);
-      oa[m] = static_cast<unsigned>(r * rsa) + 16 * lchunk(r);
-      ob[m] = static_cast<unsigned>(r * rsb) + 16 * lchunk(r);
-    }
-  }
-
-  // ga/gb: first row of the tile; rows: rows left in the piece from there
-  __device__ void load(const char *ga, const char *gb, char *la, char *lb, int64_t rows) const {
-    if (rows >= T::ROWS) {
-#pragma unroll
-      for (int m = 0; m < T::MW; ++m)
-        if (wv + 4 * m < T::NI && lon(m)) {
-          const int r0 = (wv + 4 * m) * T::RPI;
-          load_lds16(ga + oa[m], la + r0 * T::RB);
-          load_lds16(gb + ob[m], lb + r0 * T::RB);
-        }
-    } else {
-      const int last = static_cast<int>(rows - 1);
-#pragma unroll
-      for (int m = 0; m < T::MW; ++m)
-        if (wv + 4 * m < T::NI && lon(m)) {
-          const int r0 = (wv + 4 * m) * T::RPI;
-          const int r = lrow(m), rr = r < last ? r : last;
-          load_lds16(ga + rr * rsa + 16 * lchunk(r), la + r0 * T::RB);
-          load_lds16(gb + rr * rsb + 16 * lchunk(r), lb + r0 * T::RB);
-        }
-    }
-  }
-};
+constexpr int NW = kBwdWaves;  // waves per workgroup
+constexpr int NT = 64 * NW;
+constexpr int NS = kBwdStages; // tiles resident in LDS (NS - 1 in flight)
 
 // ============================ dQ (query-major) ============================
-constexpr int DQ_BQ = kDqTileQ;  // 128
+constexpr int DQ_BQ = kDqTileQ;  // 32 query rows per wave
 constexpr int DQ_BK = 64;
+static_assert(DQ_BQ == 32 * NW, "one 32-query column block per wave");
 
 template <int HD>
-__global__ __launch_bounds__(NT, 2) void dq_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
   using TL = Tile64<HD>;
   static_assert(TL::ROWS == DQ_BK, "key tiles are 64 rows");
-  constexpr int RB = TL::RB, TB = TL::TB, BUFB = 2 * TB;  // K, V
+  constexpr int RB = TL::RB, TB = TL::TB, STAGE = 2 * TB;  // K, V
   constexpr int KS = HD / 16, DT = HD / 32;
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUFB];
+  __shared__ __attribute__((aligned(16))) char smem[NS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -140,6 +60,57 @@ __global__ __launch_bounds__(NT, 2) void dq_bf16_kernel(BwdArgs a) {
   const char *kb = static_cast<const char *>(a.k) + 2 * (b * G.ks[0] + hk * G.ks[2]);
   const char *vb = static_cast<const char *>(a.v) + 2 * (b * G.vs[0] + hk * G.vs[2]);
 
+  // walk over (block, key tile)
+  struct Walk {
+    int64_t kv_start, len_kv, diag, ntiles;
+  };
+  auto walk = [&](int k) {
+    const KvRef r = ld_table(a.qkv + seg.blk_begin + k);
+    Walk w{r.kv_start, r.len_kv, r.diag_offset, 0};
+    int64_t hi = iend + r.diag_offset;
+    if (hi > r.len_kv) hi = r.len_kv;
+    w.ntiles = hi > 0 ? (hi + DQ_BK - 1) / DQ_BK : 0;
+    return w;
+  };
+  const int nblk = seg.blk_count;
+  auto first = [&](int &k_, Walk &w_) {
+    while (k_ < nblk) {
+      w_ = walk(k_);
+      if (w_.ntiles > 0) return;
+      ++k_;
+    }
+  };
+  auto next = [&](int &k_, int64_t &t_, Walk &w_) {
+    if (++t_ < w_.ntiles) return;
+    t_ = 0;
+    ++k_;
+    first(k_, w_);
+  };
+  int k = 0;
+  int64_t t = 0;
+  Walk cw{0, 0, 0, 0};
+  first(k, cw);
+
+  // K and V stream
+  const TileStream<HD, NW> ld(wave, lane, 2 * G.ks[1] * seg.stride, 2 * G.vs[1] * seg.stride);
+  const int per_tile = 2 * ld.count();
+  const unsigned lds0 = lds_addr(smem);
+  int kl = k;
+  int64_t tl_ = 0;
+  Walk lw = cw;
+  int issued = 0;
+  auto issue = [&](int stage) {
+    const int64_t jt = tl_ * DQ_BK;
+    const int64_t p0 = lw.kv_start + jt * seg.stride;
+    ld.load(kb + 2 * p0 * G.ks[1], vb + 2 * p0 * G.vs[1], lds0 + stage * STAGE,
+            lds0 + stage * STAGE + TB, lw.len_kv - jt);
+    ++issued;
+    next(kl, tl_, lw);
+  };
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (kl < nblk) issue(st);
+
   // rows past the piece read its last row; they are never stored
   bf16x8 qf[KS], df[KS];
   const int64_t row = i0w + c32;
@@ -155,65 +126,27 @@ __global__ __launch_bounds__(NT, 2) void dq_bf16_kernel(BwdArgs a) {
     }
   }
   const int64_t lr = (static_cast<int64_t>(b) * G.hq + h) * G.seqlen + pos;
-  const float lse2 = a.lse[lr] * kLog2e;
+  const float lse2 = a.lse2[lr];
   const float dd = a.dd[lr];
+  // the operands above and the first tiles have landed; from here on the only
+  // vector-memory operations in flight are the tile loads
+  vm_wait<0>();
 
   f32x16 acc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 
-  struct Walk {
-    int64_t kv_start, len_kv, diag, ntiles;
-  };
-  auto walk = [&](int k) {
-    const KvRef r = ld_table(a.qkv + seg.blk_begin + k);
-    Walk w{r.kv_start, r.len_kv, r.diag_offset, 0};
-    int64_t hi = iend + r.diag_offset;
-    if (hi > r.len_kv) hi = r.len_kv;
-    w.ntiles = hi > 0 ? (hi + DQ_BK - 1) / DQ_BK : 0;
-    return w;
-  };
-  const int nblk = seg.blk_count;
-  int k = 0;
-  Walk cw{0, 0, 0, 0};
-  while (k < nblk) {
-    cw = walk(k);
-    if (cw.ntiles > 0) break;
-    ++k;
-  }
-  // K and V rows go straight into LDS
-  const PairLoader<HD> ld(wave, lane, 2 * G.ks[1] * seg.stride, 2 * G.vs[1] * seg.stride);
-  auto gload = [&](const Walk &w, int64_t t, int buf) {
-    char *base = smem + buf * BUFB;
-    const int64_t jt = t * DQ_BK;
-    const int64_t p0 = w.kv_start + jt * seg.stride;
-    ld.load(kb + 2 * p0 * G.ks[1], vb + 2 * p0 * G.vs[1], base, base + TB, w.len_kv - jt);
-  };
-  int64_t t = 0;
-  int cur = 0;
-  if (k < nblk) gload(cw, 0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
   const int a_off = TL::a_off(lane);
   const int t_off = TL::t_off(lane);
+  int it = 0;
   while (k < nblk) {
-    int kn = k;
-    int64_t tn = t + 1;
-    Walk nw = cw;
-    if (tn >= cw.ntiles) {
-      tn = 0;
-      ++kn;
-      while (kn < nblk) {
-        nw = walk(kn);
-        if (nw.ntiles > 0) break;
-        ++kn;
-      }
-    }
-    if (kn < nblk) gload(nw, tn, cur ^ 1);
+    vm_wait((issued - 1 - it) * per_tile);  // this wave's part of tile `it` landed
+    __syncthreads();                        // every part landed; stage it-1 free
+    if (kl < nblk) issue((it + NS - 1) % NS);
 
     const int64_t j0 = t * DQ_BK;
     if (j0 <= i0w + 31 + cw.diag) {
-      const char *kt = smem + cur * BUFB;
+      const char *kt = smem + (it % NS) * STAGE;
       const char *vt = kt + TB;
       const bool need_mask = (j0 + DQ_BK - 1 > i0w + cw.diag) || (j0 + DQ_BK > cw.len_kv);
       int x = 0;
@@ -255,12 +188,8 @@ __global__ __launch_bounds__(NT, 2) void dq_bf16_kernel(BwdArgs a) {
         }
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
-    __syncthreads();
-    cur ^= 1;
-    k = kn;
-    t = tn;
-    cw = nw;
+    next(k, t, cw);
+    ++it;
   }
   if (!valid) return;
   char *ob = static_cast<char *>(a.dq) + 2 * (b * G.qs[0] + pos * G.qs[1] + h * G.qs[2]);
@@ -276,8 +205,9 @@ __global__ __launch_bounds__(NT, 2) void dq_bf16_kernel(BwdArgs a) {
 }
 
 // ========================= dK, dV (key-major) =========================
-constexpr int KV_BK = kBwdTileKV;  // 128 key rows per workgroup
+constexpr int KV_BK = kBwdTileKV;  // 32 key rows per wave
 constexpr int KV_BQ = 64;          // query rows per streamed tile
+static_assert(KV_BK == 32 * NW, "one 32-key column block per wave");
 
 // Key-major gradient kernels.  MODE 1 accumulates dV^T += dO^T P (needs S
 // only), MODE 2 accumulates dK^T += Q^T dS (needs S and dP).  Splitting the
@@ -286,15 +216,15 @@ constexpr int KV_BQ = 64;          // query rows per streamed tile
 constexpr int KV_DV = 1, KV_DK = 2;
 
 template <int HD, int MODE>
-__global__ __launch_bounds__(NT, 2) void dkdv_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
   using TL = Tile64<HD>;
   static_assert(TL::ROWS == KV_BQ, "query tiles are 64 rows");
   constexpr int RB = TL::RB;
   constexpr int TB = TL::TB;
-  constexpr int BUFB = 2 * TB + 2 * KV_BQ * 4;  // Q, dO, LSE*log2(e), D
+  constexpr int STAGE = 2 * TB + 2 * KV_BQ * 4;  // Q, dO, LSE*log2(e), D
   constexpr int KS = HD / 16, DT = HD / 32;
   constexpr bool DK = MODE == KV_DK;
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUFB];
+  __shared__ __attribute__((aligned(16))) char smem[NS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -313,22 +243,6 @@ __global__ __launch_bounds__(NT, 2) void dkdv_bf16_kernel(BwdArgs a) {
   const bool valid = col < seg.len_kv;
   const int64_t pos = seg.kv_start + (valid ? col : seg.len_kv - 1) * seg.stride;
 
-  // K (and for dK also V) as B operands of S = Q K^T and dP = dO V^T; rows
-  // past the key piece read its last row and are never stored
-  bf16x8 kf[KS], vf[DK ? KS : 1];
-  {
-    const char *ksrc = static_cast<const char *>(a.k) + 2 * (b * G.ks[0] + pos * G.ks[1] + hk * G.ks[2]);
-    const char *vsrc = static_cast<const char *>(a.v) + 2 * (b * G.vs[0] + pos * G.vs[1] + hk * G.vs[2]);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kf[ks] = __builtin_bit_cast(bf16x8, ld16(ksrc + (2 * ks + g) * 16));
-      if (DK) vf[ks] = __builtin_bit_cast(bf16x8, ld16(vsrc + (2 * ks + g) * 16));
-    }
-  }
-  f32x16 acc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
-
   // walk over (group head, block, query tile)
   struct Walk {
     int64_t q_start, len_q, diag, t0, t1;  // query tiles [t0, t1)
@@ -346,9 +260,7 @@ __global__ __launch_bounds__(NT, 2) void dkdv_bf16_kernel(BwdArgs a) {
     return w;
   };
   const int nblk = seg.blk_count, ngrp = G.group;
-  int gi = 0, k = 0;
-  Walk cw{};
-  auto advance_to_nonempty = [&](int &gi_, int &k_, Walk &w_) {
+  auto first = [&](int &gi_, int &k_, Walk &w_) {
     while (gi_ < ngrp) {
       while (k_ < nblk) {
         w_ = walk(gi_, k_);
@@ -359,65 +271,81 @@ __global__ __launch_bounds__(NT, 2) void dkdv_bf16_kernel(BwdArgs a) {
       k_ = 0;
     }
   };
-  advance_to_nonempty(gi, k, cw);
+  auto next = [&](int &gi_, int &k_, int64_t &t_, Walk &w_) {
+    if (++t_ < w_.t1) return;
+    ++k_;
+    first(gi_, k_, w_);
+    t_ = w_.t0;
+  };
+  int gi = 0, k = 0;
+  Walk cw{};
+  first(gi, k, cw);
   int64_t t = cw.t0;
 
-  float lsr = 0.f, ddr = 0.f;
-  // Q and dO rows go straight into LDS; LSE and D of the 64 rows travel
-  // through two registers.
-  const PairLoader<HD> ld(wave, lane, 2 * G.qs[1] * seg.stride, 2 * G.os[1] * seg.stride);
-  auto dload = [&](const Walk &w, int64_t tt, int buf) {
-    char *base = smem + buf * BUFB;
-    const int64_t i0 = tt * KV_BQ;
-    const char *qb = static_cast<const char *>(a.q) +
-                     2 * (b * G.qs[0] + (w.q_start + i0 * seg.stride) * G.qs[1] + w.h * G.qs[2]);
-    const char *db = static_cast<const char *>(a.dout) +
-                     2 * (b * G.os[0] + (w.q_start + i0 * seg.stride) * G.os[1] + w.h * G.os[2]);
-    ld.load(qb, db, base, base + TB, w.len_q - i0);
-    if (tid < KV_BQ) {
-      int64_t i = i0 + tid;
-      i = i < w.len_q ? i : w.len_q - 1;
-      const int64_t r = (static_cast<int64_t>(b) * G.hq + w.h) * G.seqlen + w.q_start + i * seg.stride;
-      lsr = a.lse[r] * kLog2e;
-      if (DK) ddr = a.dd[r];
+  // Q/dO stream; LSE*log2(e) and D of the 64 rows go to LDS with one 4-byte
+  // direct load each, issued by the last two waves (they have the fewest
+  // tile instructions)
+  const TileStream<HD, NW> ld(wave, lane, 2 * G.qs[1] * seg.stride, 2 * G.os[1] * seg.stride);
+  const bool stats_wave = wave >= NW - 2;
+  const int per_tile = 2 * ld.count() + (stats_wave ? 1 : 0);
+  const unsigned lds0 = lds_addr(smem);
+  int gl = gi, kl = k;
+  int64_t tl_ = t;
+  Walk lw = cw;
+  int issued = 0;
+  auto issue = [&](int stage) {
+    const int64_t i0 = tl_ * KV_BQ;
+    const int64_t p0 = lw.q_start + i0 * seg.stride;
+    const char *qb = static_cast<const char *>(a.q) + 2 * (b * G.qs[0] + p0 * G.qs[1] + lw.h * G.qs[2]);
+    const char *db = static_cast<const char *>(a.dout) + 2 * (b * G.os[0] + p0 * G.os[1] + lw.h * G.os[2]);
+    const unsigned sb = lds0 + stage * STAGE;
+    ld.load(qb, db, sb, sb + TB, lw.len_q - i0);
+    if (stats_wave) {
+      const int64_t rows = lw.len_q - i0;
+      const unsigned r = static_cast<unsigned>(lane < rows ? lane : rows - 1);
+      const int64_t row0 = (static_cast<int64_t>(b) * G.hq + lw.h) * G.seqlen + p0;
+      const float *src = wave == NW - 2 ? a.lse2 : a.dd;
+      dma4(src + row0, r * static_cast<unsigned>(seg.stride) * 4u,
+           sb + 2 * TB + (wave == NW - 2 ? 0 : KV_BQ * 4));
     }
+    ++issued;
+    next(gl, kl, tl_, lw);
   };
-  auto stats_store = [&](int buf) {
-    if (tid < KV_BQ) {
-      float *st = reinterpret_cast<float *>(smem + buf * BUFB + 2 * TB);
-      st[tid] = lsr;
-      if (DK) st[KV_BQ + tid] = ddr;
-    }
-  };
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (gl < ngrp) issue(st);
 
-  int cur = 0;
-  if (gi < ngrp) {
-    dload(cw, t, 0);
-    stats_store(0);
+  // K (and for dK also V) as B operands of S = Q K^T and dP = dO V^T; rows
+  // past the key piece read its last row and are never stored
+  bf16x8 kf[KS], vf[DK ? KS : 1];
+  {
+    const char *ksrc = static_cast<const char *>(a.k) + 2 * (b * G.ks[0] + pos * G.ks[1] + hk * G.ks[2]);
+    const char *vsrc = static_cast<const char *>(a.v) + 2 * (b * G.vs[0] + pos * G.vs[1] + hk * G.vs[2]);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kf[ks] = __builtin_bit_cast(bf16x8, ld16(ksrc + (2 * ks + g) * 16));
+      if (DK) vf[ks] = __builtin_bit_cast(bf16x8, ld16(vsrc + (2 * ks + g) * 16));
+    }
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  vm_wait<0>();
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
 
   // per-lane operand offsets (independent of the tile); loop indices only
   // add compile-time constants to them
   const int a_off = TL::a_off(lane);
   const int t_off = TL::t_off(lane);
+  int it = 0;
   while (gi < ngrp) {
-    int gn = gi, kn = k;
-    int64_t tn = t + 1;
-    Walk nw = cw;
-    if (tn >= cw.t1) {
-      ++kn;
-      advance_to_nonempty(gn, kn, nw);
-      tn = nw.t0;
-    }
-    const bool have_next = gn < ngrp;
-    if (have_next) dload(nw, tn, cur ^ 1);
+    vm_wait((issued - 1 - it) * per_tile);  // this wave's part of tile `it` landed
+    __syncthreads();                        // every part landed; stage it-1 free
+    if (gl < ngrp) issue((it + NS - 1) % NS);
 
     const int64_t qi0 = t * KV_BQ;
     // some pair of this wave visible: largest query row sees smallest key row
     if (qi0 + KV_BQ - 1 + cw.diag >= j0w) {
-      const char *qt = smem + cur * BUFB;
+      const char *qt = smem + (it % NS) * STAGE;
       const char *dt_ = qt + TB;
       const float *lt = reinterpret_cast<const float *>(qt + 2 * TB);
       const float *ddt = lt + KV_BQ;
@@ -478,14 +406,8 @@ __global__ __launch_bounds__(NT, 2) void dkdv_bf16_kernel(BwdArgs a) {
         }
       }
     }
-    if (have_next) stats_store(cur ^ 1);
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed
-    __syncthreads();
-    cur ^= 1;
-    gi = gn;
-    k = kn;
-    t = tn;
-    cw = nw;
+    next(gi, k, t, cw);
+    ++it;
   }
   if (!valid) return;
   char *out = DK ? static_cast<char *>(a.dk) + 2 * (b * G.ks[0] + pos * G.ks[1] + hk * G.ks[2])

@@ -68,6 +68,7 @@ struct BwdArgs {
   const void *q, *k, *v, *o, *dout;
   const float *lse;  // [B][Hq][N]
   float *dd;         // D = rowsum(dO*O): [B][Hq][N]
+  float *lse2;       // LSE * log2(e): [B][Hq][N]
   void *dq, *dk, *dv;
   const QSeg *qsegs;
   const KvRef *qkv;    // key pieces per query piece (dq walk)
@@ -88,8 +89,10 @@ struct MergeItem {
 constexpr int kFwdWaves = 8;                // bf16 forward: waves per workgroup
 constexpr int kFwdTileQ = 32 * kFwdWaves;   // bf16 forward: query rows per workgroup
 constexpr int kFwdStages = 4;               // bf16 forward: K/V tiles resident in LDS
-constexpr int kDqTileQ = 128;               // bf16 dq: query rows per workgroup
-constexpr int kBwdTileKV = 128;  // bf16 dk/dv: key rows per workgroup
+constexpr int kBwdWaves = 8;                // bf16 dq, dk, dv: waves per workgroup
+constexpr int kBwdStages = 4;               // bf16 dq, dk, dv: tiles resident in LDS
+constexpr int kDqTileQ = 32 * kBwdWaves;    // bf16 dq: query rows per workgroup
+constexpr int kBwdTileKV = 32 * kBwdWaves;  // bf16 dk/dv: key rows per workgroup
 constexpr int kF32TileQ = 64;    // fp32 kernels: rows per workgroup
 constexpr int kF32TileKV = 64;
 

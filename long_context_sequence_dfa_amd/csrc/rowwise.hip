@@ -167,6 +167,7 @@ __global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdArgs a) {
     }
   }
   a.dd[tid] = s;
+  a.lse2[tid] = a.lse[tid] * kLog2e;
 }
 
 inline unsigned blocks_for(int64_t threads) { return static_cast<unsigned>((threads + NT - 1) / NT); }
