@@ -10,10 +10,12 @@ resident in HBM.
 Throughput counts causal-effective FLOPs over the exact visible pairs:
 4*d per pair forward (QK^T and PV) and 10*d per pair backward (the recompute
 of S plus dP, dV, dK, dQ).  Per kernel the algorithmic share is: forward
-4*d, dK/dV kernel 8*d (S, dP, dV, dK), dQ kernel 2*d (its recompute of S and
-dP is extra work and not counted).  The dominant kernel's roofline figure
-uses that share and the kernel's own average duration, read from HIP events
-recorded on the stream right before and after it (dfa_attn_bwd_ex marks).
+4*d; dV kernel 4*d (the recompute of S, and dV); dK kernel 4*d (dP and dK);
+dQ kernel 2*d (dQ).  Recomputations beyond those five backward products (S
+again in the dK and dQ kernels, dP again in the dQ kernel) are extra work and
+not counted.  The dominant kernel's roofline figure uses that share and the
+kernel's own average duration, read from HIP events recorded on the stream
+right before and after it (dfa_attn_bwd_ex marks).
 
 Prints ONE JSON line.
 """
@@ -70,14 +72,35 @@ class HipEvents:
         return float(ms.value)
 
 
+def source_hash(kernel_file: str) -> str:
+    """sha256[:16] over a kernel source file and every header in csrc/ (the
+    kernels include all of them), so any change to the code that builds the
+    kernel changes the hash."""
+    import hashlib
+    csrc = os.path.join(ROOT, "long_context_sequence_dfa_amd", "csrc")
+    h = hashlib.sha256(open(os.path.join(csrc, kernel_file), "rb").read())
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith(".h"):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def stored_traffic(kernel: str, workload: str):
     """HBM bytes per launch of ``kernel`` from the committed counter summary
     (profiles/traffic.txt: FETCH_SIZE + WRITE_SIZE scaled by a plain copy),
-    or None when absent or when the kernel source changed since."""
-    import hashlib
+    or None when absent or when the kernel's source changed since."""
     path = os.path.join(ROOT, "profiles", "traffic.txt")
     if not os.path.exists(path):
         return None
+    for line in open(path):
+        parts = line.split()
+        if len(parts) == 4 and parts[0] == kernel and parts[1] == workload:
+            fname, want = parts[2].split(":")
+            src = os.path.join(ROOT, "long_context_sequence_dfa_amd", "csrc", fname)
+            if not os.path.exists(src) or source_hash(fname) != want:
+                return None
+            return float(parts[3])
+    return None
     for line in open(path):
         parts = line.split()
         if len(parts) == 4 and parts[0] == kernel and parts[1] == workload:
@@ -180,7 +203,7 @@ def main() -> int:
     sp = ctypes.c_void_p(stream.cuda_stream)
     ev = HipEvents()
     # per step: fwd begin, fwd end, then the backward's marks
-    ev_all = [[ev.create() for _ in range(6)] for _ in range(args.steps)]
+    ev_all = [[ev.create() for _ in range(7)] for _ in range(args.steps)]
 
     def step(m=None):
         if m is not None:
@@ -189,7 +212,7 @@ def main() -> int:
         marks = None
         if m is not None:
             ev.h.hipEventRecord(m[1], sp)
-            marks = binding.DfaKernelMarks(m[2], m[3], m[4], m[5])
+            marks = binding.DfaKernelMarks(m[2], m[3], m[4], m[5], m[6])
         dfa.dfa_attn_bwd(tq, tk, tv, o, tdo, lse, blocks, dq=dq, dk=dk, dv=dv, workspace=ws_b,
                          marks=marks)
 
@@ -209,8 +232,8 @@ def main() -> int:
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     per = {name: float(np.mean([ev.elapsed(m[a], m[b]) for m in ev_all]))
-           for name, a, b in (("fwd", 0, 1), ("bwd", 1, 5), ("bwd_pre", 2, 3), ("dq", 3, 4),
-                              ("dkdv", 4, 5))}
+           for name, a, b in (("fwd", 0, 1), ("bwd", 1, 6), ("bwd_pre", 2, 3), ("dq", 3, 4),
+                              ("dk", 4, 5), ("dv", 5, 6))}
     ms_step = elapsed * 1e3 / args.steps
     total_flops = (fwd_flops + bwd_flops) * args.steps
     value = total_flops / elapsed / 1e12
@@ -219,7 +242,8 @@ def main() -> int:
     # the dominant kernel by time, with its algorithmic FLOP share
     kernels = {"attn_fwd_bf16_fused": (per["fwd"], fwd_flops),
                "attn_bwd_dq_bf16": (per["dq"], 2.0 * D * pairs),
-               "attn_bwd_dkdv_bf16": (per["dkdv"], 8.0 * D * pairs)}
+               "attn_bwd_dk_bf16": (per["dk"], 4.0 * D * pairs),
+               "attn_bwd_dv_bf16": (per["dv"], 4.0 * D * pairs)}
     dom = max(kernels, key=lambda n: kernels[n][0])
     dom_ms, dom_flops = kernels[dom]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
@@ -244,7 +268,7 @@ def main() -> int:
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "fwd_ms": fwd_avg,
         "bwd_ms": bwd_avg,
-        "kernel_ms": {k_: per[k_] for k_ in ("fwd", "bwd_pre", "dq", "dkdv")},
+        "kernel_ms": {k_: per[k_] for k_ in ("fwd", "bwd_pre", "dq", "dk", "dv")},
         "fwd_tflops": fwd_flops / (fwd_avg * 1e-3) / 1e12,
         "bwd_tflops": bwd_flops / (bwd_avg * 1e-3) / 1e12,
         "idle_bubble_ratio": bal["bubble"],

@@ -243,13 +243,15 @@ dfa_status dfa_attn_bwd(const dfa_attn_desc *d, const dfa_block *blocks, int64_t
  * hipEvent_t (passed as void*) created by the caller; the call records it on
  * its stream right before the named kernel is launched, or (end) right after
  * its last launch.  Recording changes no result and skips no work.  The
- * backward launches, in order: D = rowsum(dO*O), the dQ kernel, the dK and
- * dV kernels (dkdv_begin is recorded before the first of the two).
+ * backward launches, in order: D = rowsum(dO*O), the dQ kernel, the dK
+ * kernel, the dV kernel.  (fp32 computes dK and dV in one kernel: dk_begin
+ * and dv_begin are then recorded back to back before it.)
  */
 typedef struct dfa_kernel_marks {
   void *pre_begin;
   void *dq_begin;
-  void *dkdv_begin;
+  void *dk_begin;
+  void *dv_begin;
   void *end;
 } dfa_kernel_marks;
 

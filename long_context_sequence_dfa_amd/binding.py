@@ -51,7 +51,8 @@ class DfaBalance(ctypes.Structure):
 
 class DfaKernelMarks(ctypes.Structure):
     _fields_ = [("pre_begin", ctypes.c_void_p), ("dq_begin", ctypes.c_void_p),
-                ("dkdv_begin", ctypes.c_void_p), ("end", ctypes.c_void_p)]
+                ("dk_begin", ctypes.c_void_p), ("dv_begin", ctypes.c_void_p),
+                ("end", ctypes.c_void_p)]
 
 
 class DfaError(RuntimeError):

@@ -438,16 +438,22 @@ hipError_t launch_bwd_dq_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dkdv_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_t s) {
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs &a, int hd, int64_t grid, int which, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (which != KV_DK && which != KV_DV) return hipErrorInvalidValue;
   const dim3 gr(static_cast<unsigned>(grid)), bl(NT);
+  const bool dk = which == KV_DK;
   if (hd == 128) {
-    hipLaunchKernelGGL((dkdv_bf16_kernel<128, KV_DK>), gr, bl, 0, s, a);
-    hipLaunchKernelGGL((dkdv_bf16_kernel<128, KV_DV>), gr, bl, 0, s, a);
+    if (dk)
+      hipLaunchKernelGGL((dkdv_bf16_kernel<128, KV_DK>), gr, bl, 0, s, a);
+    else
+      hipLaunchKernelGGL((dkdv_bf16_kernel<128, KV_DV>), gr, bl, 0, s, a);
   } else if (hd == 64) {
-    hipLaunchKernelGGL((dkdv_bf16_kernel<64, KV_DK>), gr, bl, 0, s, a);
-    hipLaunchKernelGGL((dkdv_bf16_kernel<64, KV_DV>), gr, bl, 0, s, a);
+    if (dk)
+      hipLaunchKernelGGL((dkdv_bf16_kernel<64, KV_DK>), gr, bl, 0, s, a);
+    else
+      hipLaunchKernelGGL((dkdv_bf16_kernel<64, KV_DV>), gr, bl, 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -101,7 +101,8 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int hd, int64_t grid, hipStream_t s
 hipError_t launch_fwd_f32(const FwdArgs &a, int hd, int64_t grid, hipStream_t s);
 hipError_t launch_bwd_pre(const BwdArgs &a, int dtype, int hd, hipStream_t s);
 hipError_t launch_bwd_dq_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_t s);
-hipError_t launch_bwd_dkdv_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_t s);
+// which = 2: dK kernel, 1: dV kernel
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs &a, int hd, int64_t grid, int which, hipStream_t s);
 hipError_t launch_bwd_dq_f32(const BwdArgs &a, int hd, int64_t grid, hipStream_t s);
 hipError_t launch_bwd_dkdv_f32(const BwdArgs &a, int hd, int64_t grid, hipStream_t s);
 

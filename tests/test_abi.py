@@ -41,10 +41,11 @@ def test_struct_layout_matches_header(bd, tmp_path):
 #include <stddef.h>
 #include "{HEADER}"
 int main(void) {{
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(dfa_block), sizeof(dfa_attn_desc),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(dfa_block), sizeof(dfa_attn_desc),
          offsetof(dfa_attn_desc, seqlen), offsetof(dfa_attn_desc, q_strides),
          offsetof(dfa_attn_desc, o_strides), offsetof(dfa_attn_desc, softmax_scale),
-         sizeof(dfa_balance), offsetof(dfa_balance, bubble));
+         sizeof(dfa_balance), offsetof(dfa_balance, bubble), sizeof(dfa_kernel_marks),
+         offsetof(dfa_kernel_marks, dv_begin));
   return 0;
 }}''')
     exe = tmp_path / "layout"
@@ -53,7 +54,8 @@ int main(void) {{
     D = bd.DfaAttnDesc
     assert vals == [ctypes.sizeof(bd.DfaBlock), ctypes.sizeof(D), D.seqlen.offset,
                     D.q_strides.offset, D.o_strides.offset, D.softmax_scale.offset,
-                    ctypes.sizeof(bd.DfaBalance), bd.DfaBalance.bubble.offset]
+                    ctypes.sizeof(bd.DfaBalance), bd.DfaBalance.bubble.offset,
+                    ctypes.sizeof(bd.DfaKernelMarks), bd.DfaKernelMarks.dv_begin.offset]
     assert vals[0] == 80
 
 
