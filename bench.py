@@ -231,6 +231,31 @@ def main() -> int:
         step(ev_all[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # the other forward mode, timed on its own (a few launches): the pages'
+    # per-step partial-plus-merge form when the timed mode is fused, and back
+    alt_mode = dfa.DFA_FWD_STEPWISE if mode == dfa.DFA_FWD_FUSED else dfa.DFA_FWD_FUSED
+    alt_op = dfa.DFA_OP_FWD_STEPWISE if alt_mode == dfa.DFA_FWD_STEPWISE else dfa.DFA_OP_FWD_FUSED
+    ws_alt = torch.empty(max(dfa.dfa_workspace_size(desc, blocks, alt_op), 256), dtype=torch.uint8,
+                         device=dev)
+    o_alt = torch.empty_like(tq)
+    lse_alt = torch.empty_like(lse)
+    dfa.dfa_attn_fwd(tq, tk, tv, blocks, alt_mode, o=o_alt, lse=lse_alt, workspace=ws_alt)
+    e0, e1 = ev.create(), ev.create()
+    n_alt = 3
+    ev.h.hipEventRecord(e0, sp)
+    for _ in range(n_alt):
+        dfa.dfa_attn_fwd(tq, tk, tv, blocks, alt_mode, o=o_alt, lse=lse_alt, workspace=ws_alt)
+    ev.h.hipEventRecord(e1, sp)
+    alt_ms = ev.elapsed(e0, e1) / n_alt
+    del ws_alt, o_alt, lse_alt
+
+    # measured per-(rank, step) slot times of the forward: the idle bubble a
+    # synchronous ring of P devices would see with these block costs
+    from long_context_sequence_dfa_amd import timeline
+    full = dfa.dfa_schedule_build(wl["kind"], N, wl["P"])  # every rank, also for a rank's share
+    slot_ms = timeline.rank_step_times(tq, tk, tv, full, wl["P"], repeats=3, stream=stream)
+    bubble_measured = timeline.measured_balance(slot_ms)["bubble"]
+
     per = {name: float(np.mean([ev.elapsed(m[a], m[b]) for m in ev_all]))
            for name, a, b in (("fwd", 0, 1), ("bwd", 1, 6), ("bwd_pre", 2, 3), ("dq", 3, 4),
                               ("dk", 4, 5), ("dv", 5, 6))}
@@ -270,8 +295,11 @@ def main() -> int:
         "bwd_ms": bwd_avg,
         "kernel_ms": {k_: per[k_] for k_ in ("fwd", "bwd_pre", "dq", "dk", "dv")},
         "fwd_tflops": fwd_flops / (fwd_avg * 1e-3) / 1e12,
+        f"fwd_{'stepwise' if mode == dfa.DFA_FWD_FUSED else 'fused'}_ms": alt_ms,
+        f"fwd_{'stepwise' if mode == dfa.DFA_FWD_FUSED else 'fused'}_tflops": fwd_flops / (alt_ms * 1e-3) / 1e12,
         "bwd_tflops": bwd_flops / (bwd_avg * 1e-3) / 1e12,
         "idle_bubble_ratio": bal["bubble"],
+        "idle_bubble_ratio_measured": bubble_measured,
         "comm_latency_ms": 0.0,
         "config": {"workload": args.workload, "global_batch": B, "seq_len": N, "heads_q": Hq,
                    "heads_kv": Hkv, "head_dim": D,

@@ -2,7 +2,8 @@
 
 The compute path is the C-ABI library ``libdfa.so`` (hand-written HIP);
 ``binding`` marshals torch tensors into it.  ``inputs`` holds the seeded
-synthetic input generator.
+synthetic input generator; ``timeline`` times each (rank, step) slot of a
+schedule on its own (measured idle bubble).
 """
 from .binding import (  # noqa: F401
     DFA_BF16, DFA_F32, DFA_FWD_FUSED, DFA_FWD_STEPWISE, DFA_OP_BWD, DFA_OP_FWD_FUSED,

@@ -1,0 +1,68 @@
+"""Measured per-virtual-rank timeline of one forward pass.
+
+The pages judge a schedule by how long each rank computes at each ring step:
+a step lasts as long as its slowest rank, and the time the other ranks wait
+is the idle bubble (DistFlashAttn paper record, "Core Innovation 1" and its
+utilisation figure; Striped Attention Guide, "Why Striping Solves Load
+Imbalance").  On one GPU every (rank, step) slot can be timed on its own:
+each block of the slot runs alone through dfa_attn_block_fwd between two
+events on the stream, and the slot's time is the sum over its blocks.  The
+same slot times, combined the way a synchronous ring combines them, give
+the measured counterpart of the pair-count balance that
+dfa_schedule_balance computes from the block list.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import binding
+
+
+def rank_step_times(q, k, v, blocks, n_ranks: int, repeats: int = 3, scale=None, stream=None):
+    """Milliseconds per (rank, step) slot, shape [n_ranks, n_ranks]: each block
+    timed alone (median of ``repeats`` launches after one warm-up launch),
+    summed over the blocks of its slot.  Slots without blocks cost 0."""
+    import torch
+    arr = np.ascontiguousarray(blocks, dtype=np.int64).reshape(-1, 10)
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    B, _, Hq, D = q.shape
+    times = np.zeros((n_ranks, n_ranks), dtype=np.float64)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * repeats)]
+    for blk in arr:
+        rank, step, len_q = int(blk[0]), int(blk[1]), int(blk[5])
+        op = torch.empty((B, Hq, len_q, D), dtype=torch.float32, device=q.device)
+        lp = torch.empty((B, Hq, len_q), dtype=torch.float32, device=q.device)
+        binding.dfa_attn_block_fwd(q, k, v, blk, op, lp, scale=scale, stream=stream)
+        for r in range(repeats):
+            ev[2 * r].record(stream)
+            binding.dfa_attn_block_fwd(q, k, v, blk, op, lp, scale=scale, stream=stream)
+            ev[2 * r + 1].record(stream)
+        stream.synchronize()
+        times[rank, step] += float(np.median([ev[2 * r].elapsed_time(ev[2 * r + 1])
+                                              for r in range(repeats)]))
+    return times
+
+
+def measured_balance(times) -> dict:
+    """Synchronous-ring accounting of slot costs ``times[rank, step]``: per-rank
+    busy time, per-step maximum, makespan (sum of the step maxima) and the
+    idle bubble 1 - sum(times) / (P * makespan)."""
+    t = np.asarray(times, dtype=np.float64)
+    P = t.shape[0]
+    step_max = t.max(axis=0)
+    makespan = float(step_max.sum())
+    busy = float(t.sum())
+    bubble = 1.0 - busy / (P * makespan) if makespan > 0 else 0.0
+    return {"rank_busy": t.sum(axis=1), "step_max": step_max, "makespan": makespan,
+            "busy": busy, "bubble": bubble}
+
+
+def pair_times(blocks, n_ranks: int):
+    """The pair counts of the block list in the same [rank, step] layout (the
+    cost model in which dfa_schedule_balance measures the bubble)."""
+    arr = np.ascontiguousarray(blocks, dtype=np.int64).reshape(-1, 10)
+    t = np.zeros((n_ranks, n_ranks), dtype=np.float64)
+    for blk in arr:
+        t[int(blk[0]), int(blk[1])] += float(blk[9])
+    return t

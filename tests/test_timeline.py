@@ -1,0 +1,53 @@
+"""Measured per-virtual-rank timeline: the ring accounting of slot costs
+(long_context_sequence_dfa_amd.timeline) against the pair-count balance the
+library computes, and on the GPU the measured bubbles of the three schedules.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from long_context_sequence_dfa_amd import binding, timeline
+
+
+@pytest.mark.parametrize("kind,N,P", [(0, 1024, 4), (1, 4096, 8), (2, 2048, 8), (0, 65536, 16)])
+def test_pair_costs_reproduce_the_computed_bubble(kind, N, P):
+    # with pair counts as slot costs, the synchronous-ring accounting is the
+    # library's own balance figure
+    blocks = binding.dfa_schedule_build(kind, N, P)
+    t = timeline.pair_times(blocks, P)
+    m = timeline.measured_balance(t)
+    bal = binding.dfa_schedule_balance(blocks, P)
+    assert m["busy"] == bal["total_pairs"]
+    assert np.array_equal(m["rank_busy"].astype(np.int64), bal["rank_pairs"])
+    assert np.array_equal(m["step_max"].astype(np.int64), bal["step_max"])
+    assert math.isclose(m["bubble"], bal["bubble"], rel_tol=0, abs_tol=1e-12)
+
+
+def test_measured_balance_closed_forms():
+    # equal slots: no bubble; one busy rank per step: bubble 1 - 1/P
+    assert timeline.measured_balance(np.ones((4, 4)))["bubble"] == 0.0
+    assert math.isclose(timeline.measured_balance(np.eye(5))["bubble"], 1 - 1 / 5)
+    assert timeline.measured_balance(np.zeros((3, 3)))["bubble"] == 0.0
+
+
+@pytest.mark.gpu
+def test_measured_bubbles_of_the_three_schedules():
+    import torch
+    from long_context_sequence_dfa_amd import inputs
+    N, P, H, D = 16384, 8, 32, 128
+    q, k, v = inputs.workload_tensors(1003, 1, N, H, H, D, "bf16", 1 / math.sqrt(D))
+    tq, tk, tv = (inputs.to_torch(x, "bf16", "cuda") for x in (q, k, v))
+    out = {}
+    for kind in (0, 1, 2):
+        blocks = binding.dfa_schedule_build(kind, N, P)
+        t = timeline.rank_step_times(tq, tk, tv, blocks, P, repeats=2)
+        assert (t >= 0).all() and t.sum() > 0
+        out[kind] = timeline.measured_balance(t)["bubble"]
+        print(f"schedule {kind}: measured bubble {out[kind]:.3f}, computed "
+              f"{binding.dfa_schedule_balance(blocks, P)['bubble']:.3f}", flush=True)
+    # the contiguous ring leaves ranks idle while the diagonal's owner works;
+    # folding and striping spread the causal triangle evenly
+    assert out[0] > 0.3
+    assert out[1] < 0.2 and out[2] < 0.2
+    assert out[0] > 2 * max(out[1], out[2])
