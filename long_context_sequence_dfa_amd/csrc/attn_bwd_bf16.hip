@@ -160,12 +160,16 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {  // two halves of 32 keys
         f32x16 sv = f32x16{}, pv = f32x16{};
+        // the S/dP products at raised issue priority: while this wave feeds
+        // the matrix core, the SIMD's other wave fills the VALU slots
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const int o = a_off + 32 * kh * RB + ks * 32;
           sv = mfma32(__builtin_bit_cast(bf16x8, ld16(kt + o)), qf[ks], sv);
           pv = mfma32(__builtin_bit_cast(bf16x8, ld16(vt + o)), df[ks], pv);
         }
+        __builtin_amdgcn_s_setprio(0);
         if (need_mask) {
 #pragma unroll
           for (int i = 0; i < 16; ++i)
@@ -361,11 +365,13 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
       for (int mt = 0; mt < 2; ++mt) {  // two halves of 32 query rows
         f32x16 s = f32x16{}, dpm = f32x16{};
         const char *qa = qt + a_off + 32 * mt * RB, *da = dt_ + a_off + 32 * mt * RB;
+        __builtin_amdgcn_s_setprio(1);  // see the dQ kernel
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           s = mfma32(__builtin_bit_cast(bf16x8, ld16(qa + ks * 32)), kf[ks], s);
           if (DK) dpm = mfma32(__builtin_bit_cast(bf16x8, ld16(da + ks * 32)), vf[ks], dpm);
         }
+        __builtin_amdgcn_s_setprio(0);
         // element i is query row qi0 + 32mt + 16(i/8) + 8g + i%8; masked
         // scores become -inf (probability 0)
         if (need_mask) {

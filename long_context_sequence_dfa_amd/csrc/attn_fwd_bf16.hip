@@ -185,11 +185,15 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
       const char *kt = smem + (it % NS) * STAGE;
       const char *vt = kt + TB;
       f32x16 s0 = f32x16{}, s1 = f32x16{};
+      // S at raised issue priority: while this wave feeds the matrix core,
+      // the SIMD's other wave fills the VALU slots with its softmax
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         s0 = mfma32(__builtin_bit_cast(bf16x8, ld16(kt + a_off + ks * 32)), qf[ks], s0);
         s1 = mfma32(__builtin_bit_cast(bf16x8, ld16(kt + a_off + 32 * RB + ks * 32)), qf[ks], s1);
       }
+      __builtin_amdgcn_s_setprio(0);
       // element i of s0 / s1 is key j0 + 32*(i/16) + 16*((i%16)/8) + 8g + i%8
       if ((j0 + BK - 1 > i0w + cw.diag) || (j0 + BK > cw.len_kv)) {
         // key j0 + jj is visible iff jj <= lim; x = 8g - lim
@@ -204,13 +208,16 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
           if (x + kc + 32 > 0) s1[i] = -INFINITY;
         }
       }
-      float mx = fmaxf(s0[0], s1[0]);
+      // row max with the NaN-propagating maximum: v_maximum3_f32 needs no
+      // operand canonicalisation (the scores hold no NaN; -inf is kept)
+      float mx = __builtin_elementwise_maximum(s0[0], s1[0]);
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-      mx = fmaxf(mx, wave_swap32(mx)) * c;
+      for (int i = 1; i < 16; ++i)
+        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[i], s1[i]));
+      mx = __builtin_elementwise_maximum(mx, wave_swap32(mx)) * c;
       // raise the reference max only when it grows by more than TAU: P <= 2^TAU
       if (__any(mx > m_run + TAU)) {
-        const float m_new = fmaxf(m_run, mx);
+        const float m_new = __builtin_elementwise_maximum(m_run, mx);
         // 1 for rows whose max did not rise (also all-masked rows: no -inf - -inf);
         // 0 when a row sees its first key
         const float alpha = m_new > m_run ? fast_exp2(m_run - m_new) : 1.f;
