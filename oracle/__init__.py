@@ -48,7 +48,7 @@ def _load():
             lib = ctypes.CDLL(_LIB_PATH)
             i64, f64, p = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
             lib.orc_attn_rows.argtypes = [i64] * 5 + [f64] + [p] * 3 + [i64, p, i64, p, p, p]
-            lib.orc_block_partial.argtypes = [i64] * 5 + [f64] + [p] * 3 + [i64] * 5 + [p, p]
+            lib.orc_block_partial.argtypes = [i64] * 5 + [f64] + [p] * 3 + [i64] * 6 + [p, p]
             lib.orc_merge.argtypes = [i64, i64, i64, p, p, p, p]
             lib.orc_grad_rows.argtypes = [i64] * 5 + [f64] + [p] * 4 + [i64, p, i64, p] + [p] * 5
             lib.orc_grad_cols.argtypes = ([i64] * 5 + [f64] + [p] * 4 + [i64, p, p, p]
@@ -104,15 +104,17 @@ def attn_rows(q, k, v, scale, rows=None, heads=None):
     return o, lse
 
 
-def block_partial(q, k, v, scale, q_start, kv_start, len_q, len_kv, stride):
-    """O2: one block's normalised partial.  Returns o [B, Hq, len_q, d], lse [B, Hq, len_q]."""
+def block_partial(q, k, v, scale, q_start, kv_start, len_q, len_kv, stride, run=1):
+    """O2: one block's normalised partial.  Local row i of either piece sits at
+    start + (i // run) * stride + i % run.  Returns o [B, Hq, len_q, d],
+    lse [B, Hq, len_q]."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, N, Hq, Hkv, d = _dims(q, k)
     o = np.zeros((B, Hq, len_q, d))
     lse = np.zeros((B, Hq, len_q))
     _check(_load().orc_block_partial(B, N, Hq, Hkv, d, float(scale), _ptr(q), _ptr(k), _ptr(v),
                                      int(q_start), int(kv_start), int(len_q), int(len_kv),
-                                     int(stride), _ptr(o), _ptr(lse)), "block_partial")
+                                     int(stride), int(run), _ptr(o), _ptr(lse)), "block_partial")
     return o, lse
 
 

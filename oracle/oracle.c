@@ -134,22 +134,34 @@ int orc_attn_rows(int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int64_t d, doub
   return err;
 }
 
+/* position of local row i of a shard: runs of `run` consecutive tokens,
+ * consecutive runs `stride` apart (run 1: start + i*stride; stripe blocks of
+ * B tokens over P ranks: run B, stride P*B -- Striped Attention Guide,
+ * "Mathematical Formulation of Token Striping", block-striped set) */
+static int64_t piece_position(int64_t start, int64_t stride, int64_t run, int64_t i) {
+  return start + (i / run) * stride + i % run;
+}
+
 /*
- * O2 -- partial attention of one (query-chunk, key-chunk) block.
- * Query row i of the block sits at global position q_start + i*stride, key
- * row j at kv_start + j*stride.  Key j is visible to query i iff its global
- * position is not after the query's (GlobalPos rule).  Each row is normalised
- * over the block's visible keys only.
+ * O2 -- partial attention of one (query-shard, key-shard) block.
+ * Query row i of the block sits at global position
+ * piece_position(q_start, stride, run, i), key row j at
+ * piece_position(kv_start, stride, run, j).  Key j is visible to query i iff
+ * its global position is not after the query's (GlobalPos rule).  Each row is
+ * normalised over the block's visible keys only.
  *   o_part : [B][Hq][len_q][d]     lse_part : [B][Hq][len_q]
  */
+
 int orc_block_partial(int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int64_t d, double scale,
                       const double *q, const double *k, const double *v,
                       int64_t q_start, int64_t kv_start, int64_t len_q, int64_t len_kv,
-                      int64_t stride, double *o_part, double *lse_part) {
-  if (!dims_ok(B, N, Hq, Hkv, d) || stride < 1 || len_q < 0 || len_kv < 0) return ORC_EARG;
+                      int64_t stride, int64_t run, double *o_part, double *lse_part) {
+  if (!dims_ok(B, N, Hq, Hkv, d) || stride < 1 || run < 1 || len_q < 0 || len_kv < 0)
+    return ORC_EARG;
+  if (run > 1 && stride < run) return ORC_EARG;
   if (q_start < 0 || kv_start < 0) return ORC_EARG;
-  if (len_q > 0 && q_start + (len_q - 1) * stride >= N) return ORC_EARG;
-  if (len_kv > 0 && kv_start + (len_kv - 1) * stride >= N) return ORC_EARG;
+  if (len_q > 0 && piece_position(q_start, stride, run, len_q - 1) >= N) return ORC_EARG;
+  if (len_kv > 0 && piece_position(kv_start, stride, run, len_kv - 1) >= N) return ORC_EARG;
   int64_t group = Hq / Hkv;
   int err = ORC_OK;
   int64_t total = B * Hq * len_q;
@@ -164,9 +176,9 @@ int orc_block_partial(int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int64_t d, 
 #pragma omp for schedule(dynamic, 1)
       for (int64_t w = 0; w < total; ++w) {
         int64_t b = w / (Hq * len_q), h = (w / len_q) % Hq, i = w % len_q;
-        int64_t qpos = q_start + i * stride, nk = 0;
+        int64_t qpos = piece_position(q_start, stride, run, i), nk = 0;
         for (int64_t j = 0; j < len_kv; ++j) {
-          int64_t kpos = kv_start + j * stride;
+          int64_t kpos = piece_position(kv_start, stride, run, j);
           if (kpos <= qpos) keys[nk++] = kpos;
         }
         const double *qi = vec(q, N, Hq, d, b, qpos, h);

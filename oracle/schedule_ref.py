@@ -16,6 +16,8 @@ Definitions taken from the pages:
   Assignment", and the worker listing's folded chunk indices).
 * STRIPED -- rank p owns the positions i with i mod P == p (Striped Attention
   Guide, "Mathematical Formulation of Token Striping", first set).
+* STRIPED_BLOCK (stripe B) -- rank p owns the positions i with
+  floor(i / B) mod P == p (the same section, block-striped set).
 * Ring rotation -- at step s rank p holds the key/value shard of rank
   (p - s) mod P: shards move to rank p+1 each step (Striped Attention Guide,
   "Workload Balance Theorem"; DistFlashAttn worker listing, next/prev ranks).
@@ -24,50 +26,68 @@ Definitions taken from the pages:
   of "Algorithmic Mechanics" 1, step 2).
 
 A block is one (query piece of rank p) x (key piece of rank (p-s) mod P) with
-at least one visible pair.  A piece is an arithmetic run of positions
-start, start+stride, ...: RING has one piece per rank, BALANCED two (its low
-and high chunk), STRIPED one with stride P.
+at least one visible pair.  A piece is a sorted list of positions, described
+by (start, length, stride, run): runs of `run` consecutive positions, runs
+`stride` apart.  RING has one piece per rank, BALANCED two (its low and high
+chunk), STRIPED one with stride P (run 1), STRIPED_BLOCK one with stride P*B
+and run B; the description is checked against the listed positions.
 
-Block record (10 little-endian int64): rank, step, kv_rank, q_start, kv_start,
-len_q, len_kv, stride, diag_offset, pairs.  diag_offset is the integer o with
-"local key j visible to local query i iff j <= i + o"; when several o fit (a
-block where every pair is visible) the record uses floor((q_start-kv_start)/stride).
+Block record (11 little-endian int64): rank, step, kv_rank, q_start, kv_start,
+len_q, len_kv, stride, diag_offset, pairs, run.  For run 1, diag_offset is the
+integer o with "local key j visible to local query i iff j <= i + o"; when
+several o fit (a block where every pair is visible) the record uses
+floor((q_start-kv_start)/stride).  For run > 1 visibility is not one shifted
+diagonal and the record carries floor((q_start-kv_start)/stride) as well.
 Blocks are listed in (rank, step, q_start, kv_start) order.
 """
 from __future__ import annotations
 
 import numpy as np
 
-RING, BALANCED, STRIPED = 0, 1, 2
-KIND_NAMES = {RING: "ring", BALANCED: "balanced", STRIPED: "striped"}
+RING, BALANCED, STRIPED, STRIPED_BLOCK = 0, 1, 2, 3
+KIND_NAMES = {RING: "ring", BALANCED: "balanced", STRIPED: "striped",
+              STRIPED_BLOCK: "striped_block"}
 FIELDS = ("rank", "step", "kv_rank", "q_start", "kv_start", "len_q", "len_kv",
-          "stride", "diag_offset", "pairs")
+          "stride", "diag_offset", "pairs", "run")
 
 
-def rank_pieces(kind: int, n: int, p: int):
-    """List, per rank, of its (start, length, stride) position runs."""
+def rank_pieces(kind: int, n: int, p: int, stripe: int = 1):
+    """List, per rank, of its (start, length, stride, run) position runs."""
     if p < 1 or n < 1:
         raise ValueError("need N >= 1 and P >= 1")
     if kind == RING:
         if n % p:
             raise ValueError("P must divide N")
         c = n // p
-        return [[(r * c, c, 1)] for r in range(p)]
+        return [[(r * c, c, 1, 1)] for r in range(p)]
     if kind == BALANCED:
         if n % (2 * p):
             raise ValueError("2P must divide N")
         c = n // (2 * p)
-        return [[(r * c, c, 1), ((2 * p - 1 - r) * c, c, 1)] for r in range(p)]
+        return [[(r * c, c, 1, 1), ((2 * p - 1 - r) * c, c, 1, 1)] for r in range(p)]
     if kind == STRIPED:
         if n % p:
             raise ValueError("P must divide N")
-        return [[(r, n // p, p)] for r in range(p)]
+        return [[(r, n // p, p, 1)] for r in range(p)]
+    if kind == STRIPED_BLOCK:
+        if stripe < 1 or n % (p * stripe):
+            raise ValueError("P * stripe must divide N")
+        out = []
+        for r in range(p):
+            # the definition, listed: positions whose stripe block belongs to r
+            own = np.nonzero((np.arange(n, dtype=np.int64) // stripe) % p == r)[0]
+            piece = (int(own[0]), int(own.size), p * stripe, stripe)
+            if not np.array_equal(positions(piece), own):
+                raise AssertionError("stripe-block piece description does not list its positions")
+            out.append([piece])
+        return out
     raise ValueError("unknown schedule kind")
 
 
 def positions(piece) -> np.ndarray:
-    start, length, stride = piece
-    return start + stride * np.arange(length, dtype=np.int64)
+    start, length, stride, run = piece
+    i = np.arange(length, dtype=np.int64)
+    return start + (i // run) * stride + i % run
 
 
 def _diag_offset(qpos: np.ndarray, kpos: np.ndarray, q_start, kv_start, stride) -> int:
@@ -93,9 +113,9 @@ def _diag_offset(qpos: np.ndarray, kpos: np.ndarray, q_start, kv_start, stride) 
     return conventional
 
 
-def enumerate_schedule(kind: int, n: int, p: int) -> np.ndarray:
-    """All non-empty blocks of a schedule as an int64 array [n_blocks, 10]."""
-    pieces = rank_pieces(kind, n, p)
+def enumerate_schedule(kind: int, n: int, p: int, stripe: int = 1) -> np.ndarray:
+    """All non-empty blocks of a schedule as an int64 array [n_blocks, 11]."""
+    pieces = rank_pieces(kind, n, p, stripe)
     out = []
     for r in range(p):
         for s in range(p):
@@ -106,10 +126,13 @@ def enumerate_schedule(kind: int, n: int, p: int) -> np.ndarray:
                     pairs = int(np.searchsorted(kpos, qpos, side="right").sum())
                     if pairs == 0:
                         continue
-                    off = _diag_offset(qpos, kpos, qp[0], kp[0], qp[2])
-                    out.append((r, s, j, qp[0], kp[0], qp[1], kp[1], qp[2], off, pairs))
+                    if qp[3] == 1:
+                        off = _diag_offset(qpos, kpos, qp[0], kp[0], qp[2])
+                    else:
+                        off = (qp[0] - kp[0]) // qp[2]
+                    out.append((r, s, j, qp[0], kp[0], qp[1], kp[1], qp[2], off, pairs, qp[3]))
     out.sort(key=lambda t: (t[0], t[1], t[3], t[4]))
-    return np.array(out, dtype=np.int64).reshape(-1, 10)
+    return np.array(out, dtype=np.int64).reshape(-1, 11)
 
 
 def to_bytes(blocks: np.ndarray) -> bytes:

@@ -172,21 +172,25 @@ def test_error_magnitudes_bound_the_gradients(orc):
     np.testing.assert_allclose(a[2], dv_absdo, atol=1e-12)
 
 
-@pytest.mark.parametrize("kind,N,P", [(sr.RING, 24, 4), (sr.BALANCED, 24, 3), (sr.STRIPED, 24, 4),
-                                      (sr.STRIPED, 24, 6), (sr.BALANCED, 16, 8), (sr.RING, 7, 7)])
-def test_merged_block_partials_equal_full_attention(orc, kind, N, P):
+@pytest.mark.parametrize("kind,N,P,stripe", [(sr.RING, 24, 4, 1), (sr.BALANCED, 24, 3, 1),
+                                             (sr.STRIPED, 24, 4, 1), (sr.STRIPED, 24, 6, 1),
+                                             (sr.BALANCED, 16, 8, 1), (sr.RING, 7, 7, 1),
+                                             (sr.STRIPED_BLOCK, 24, 3, 2), (sr.STRIPED_BLOCK, 32, 2, 4),
+                                             (sr.STRIPED_BLOCK, 30, 2, 5)])
+def test_merged_block_partials_equal_full_attention(orc, kind, N, P, stripe):
     """The pages' exactness claim: merging every block of any schedule gives
-    monolithic causal attention."""
+    monolithic causal attention (also for stripe blocks, where a block's
+    visibility is no single shifted diagonal)."""
     B, Hq, Hkv, d = 2, 2, 1, 4
     q, k, v = rand(B, N, Hq, d), rand(B, N, Hkv, d), rand(B, N, Hkv, d)
     scale = 0.6
     full_o, full_l = orc.attn_rows(q, k, v, scale)
-    blocks = sr.enumerate_schedule(kind, N, P)
+    blocks = sr.enumerate_schedule(kind, N, P, stripe)
     merged_o = np.zeros_like(full_o)
     merged_l = np.full_like(full_l, -np.inf)
     for b in blocks:
-        op, lp = orc.block_partial(q, k, v, scale, b[3], b[4], b[5], b[6], b[7])
-        rows = b[3] + b[7] * np.arange(b[5])
+        op, lp = orc.block_partial(q, k, v, scale, b[3], b[4], b[5], b[6], b[7], b[10])
+        rows = sr.positions((b[3], b[5], b[7], b[10]))
         acc_o, acc_l = merged_o[:, :, rows], merged_l[:, :, rows]
         mo, ml = orc.merge(np.stack([acc_o, op]), np.stack([acc_l, lp]))
         merged_o[:, :, rows], merged_l[:, :, rows] = mo, ml
