@@ -91,13 +91,16 @@ enum {
 enum { DFA_OP_FWD_FUSED = 0, DFA_OP_FWD_STEPWISE = 1, DFA_OP_BWD = 2 };
 
 /*
- * One block of a schedule: the queries of one chunk of rank `rank` against
- * the keys of one chunk of rank `kv_rank` at ring step `step`.  Ten
- * little-endian int64 fields (80 bytes).  Local query row i sits at global
- * position q_start + i*stride, local key row j at kv_start + j*stride; key j
- * is visible to query i iff j <= i + diag_offset, which is the same as "the
- * key's global position is not after the query's".  Only blocks with at least
- * one visible pair exist.
+ * One block of a schedule: the queries of one shard of rank `rank` against
+ * the keys of one shard of rank `kv_rank` at ring step `step`.  Eleven
+ * little-endian int64 fields (88 bytes).  A shard is a sequence of runs of
+ * `run` consecutive tokens, consecutive runs `stride` apart: local row i sits
+ * at global position start + (i / run) * stride + i % run.  run = 1 gives the
+ * rows start + i * stride (contiguous chunks: stride 1; token stripes:
+ * stride P); block stripes of B tokens have run = B, stride = P * B.  Key j is
+ * visible to query i iff its global position is not after the query's; for
+ * run = 1 that is j <= i + diag_offset.  Only blocks with at least one visible
+ * pair exist.
  */
 typedef struct dfa_block {
   int64_t rank;        /* virtual rank computing the block (owns the query rows) */
@@ -107,9 +110,11 @@ typedef struct dfa_block {
   int64_t kv_start;    /* global position of local key row 0 */
   int64_t len_q;       /* number of query rows */
   int64_t len_kv;      /* number of key rows */
-  int64_t stride;      /* global distance between consecutive rows: 1, or P when striped */
+  int64_t stride;      /* global distance between consecutive runs: 1 (chunks), P (token
+                          stripes), P * B (block stripes) */
   int64_t diag_offset; /* floor((q_start - kv_start) / stride) */
   int64_t pairs;       /* number of visible (query, key) pairs */
+  int64_t run;         /* consecutive tokens per run: 1, or B for block stripes */
 } dfa_block;
 
 /*
@@ -172,6 +177,22 @@ dfa_status dfa_schedule_build(int32_t kind, int64_t seqlen, int32_t n_ranks, dfa
                               int64_t capacity, int64_t *n_out);
 
 /*
+ * dfa_schedule_build_striped_blocks -- the striped schedule with stripe blocks
+ * of `stripe` tokens (host only): rank p owns the tokens i with
+ * floor(i / stripe) = p (mod P) (Striped Attention Guide, "Mathematical
+ * Formulation of Token Striping", block-striped variant, and its "Block
+ * Stripe Size" recommendation of 64 or 128).  At step s rank r holds the keys
+ * of rank (r - s) mod P, as in DFA_SCHED_STRIPED.  Blocks have run = stripe and
+ * stride = P * stride; stripe = 1 reproduces DFA_SCHED_STRIPED exactly.
+ *   seqlen : N with N % (n_ranks * stripe) == 0, else DFA_E_SHAPE.
+ *   stripe : >= 1.  The attention calls take run = 1 or run % 64 == 0 (their
+ *            row tiles are 64 rows); other stripes are only enumerated.
+ * Other arguments as dfa_schedule_build.
+ */
+dfa_status dfa_schedule_build_striped_blocks(int64_t seqlen, int32_t n_ranks, int64_t stripe,
+                                             dfa_block *out, int64_t capacity, int64_t *n_out);
+
+/*
  * dfa_schedule_balance -- per-rank and per-step loads of a block list (host).
  *   rank_pairs, step_max : host arrays of n_ranks int64, or NULL.
  *   out                  : receives the totals (may be NULL).
@@ -209,7 +230,7 @@ dfa_status dfa_lse_merge(int64_t n_rows, int32_t head_dim, float *o_acc, float *
  * dfa_attn_fwd -- forward over a block list (a whole schedule or any subset,
  * e.g. one rank's share).
  *   blocks/n_blocks : host array (as built by dfa_schedule_build or a subset).
- *                     The distinct query pieces (q_start, len_q, stride) must
+ *                     The distinct query pieces (q_start, len_q, stride, run) must
  *                     not share rows, nor the distinct key pieces.
  *   mode            : DFA_FWD_FUSED or DFA_FWD_STEPWISE.
  *   o               : device, dtype, strides o_strides.
@@ -230,8 +251,9 @@ dfa_status dfa_attn_fwd(const dfa_attn_desc *d, const dfa_block *blocks, int64_t
  *                 block touches are written as 0.  For grouped-query
  *                 attention dk and dv sum over the query heads of a group.
  * bf16 only: 64 consecutive rows of one piece must span less than 2^31
- * bytes in each of q, k, v and d_o (64 * 2 * token stride * piece stride),
- * else DFA_E_UNSUPPORTED.
+ * bytes in each of q, k, v and d_o (64 * 2 * token stride * row step, the row
+ * step being the block's stride for run = 1 and 1 otherwise), else
+ * DFA_E_UNSUPPORTED.
  */
 dfa_status dfa_attn_bwd(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n_blocks,
                         const void *q, const void *k, const void *v, const void *o,

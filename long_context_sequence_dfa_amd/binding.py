@@ -24,11 +24,13 @@ DFA_F32, DFA_BF16 = 0, 1
 DFA_FWD_FUSED, DFA_FWD_STEPWISE = 0, 1
 DFA_OP_FWD_FUSED, DFA_OP_FWD_STEPWISE, DFA_OP_BWD = 0, 1, 2
 
-EXPORTED = ("dfa_schedule_build", "dfa_schedule_balance", "dfa_attn_block_fwd", "dfa_lse_merge",
+EXPORTED = ("dfa_schedule_build", "dfa_schedule_build_striped_blocks", "dfa_schedule_balance",
+            "dfa_attn_block_fwd", "dfa_lse_merge",
             "dfa_attn_fwd", "dfa_attn_bwd", "dfa_attn_bwd_ex", "dfa_workspace_size",
             "dfa_status_string")
 BLOCK_FIELDS = ("rank", "step", "kv_rank", "q_start", "kv_start", "len_q", "len_kv", "stride",
-                "diag_offset", "pairs")
+                "diag_offset", "pairs", "run")
+NB = len(BLOCK_FIELDS)
 
 
 class DfaBlock(ctypes.Structure):
@@ -76,6 +78,7 @@ def lib() -> ctypes.CDLL:
             L = ctypes.CDLL(LIB_PATH)
             i32, i64, p, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
             L.dfa_schedule_build.argtypes = [i32, i64, i32, p, i64, ctypes.POINTER(i64)]
+            L.dfa_schedule_build_striped_blocks.argtypes = [i64, i32, i64, p, i64, ctypes.POINTER(i64)]
             L.dfa_schedule_balance.argtypes = [p, i64, i32, p, p, p]
             L.dfa_attn_block_fwd.argtypes = [p, p, p, p, p, p, p, p]
             L.dfa_lse_merge.argtypes = [i64, i32, p, p, p, p, p]
@@ -106,21 +109,40 @@ def _check(st: int, what: str) -> None:
 
 # ---------------------------------------------------------------- schedules
 def dfa_schedule_build(kind: int, seqlen: int, n_ranks: int) -> np.ndarray:
-    """Blocks of a schedule as an int64 array [n_blocks, 10] (dfa_block fields)."""
+    """Blocks of a schedule as an int64 array [n_blocks, 11] (dfa_block fields)."""
     L = lib()
     n = ctypes.c_int64(0)
     _check(L.dfa_schedule_build(int(kind), int(seqlen), int(n_ranks), None, 0, ctypes.byref(n)),
            "dfa_schedule_build")
-    out = np.zeros((n.value, 10), dtype=np.int64)
+    out = np.zeros((n.value, NB), dtype=np.int64)
     _check(L.dfa_schedule_build(int(kind), int(seqlen), int(n_ranks),
                                 out.ctypes.data_as(ctypes.c_void_p), n.value, ctypes.byref(n)),
            "dfa_schedule_build")
     return out
 
 
+def dfa_schedule_build_striped_blocks(seqlen: int, n_ranks: int, stripe: int) -> np.ndarray:
+    """The striped schedule with stripe blocks of ``stripe`` tokens, [n_blocks, 11]."""
+    L = lib()
+    n = ctypes.c_int64(0)
+    _check(L.dfa_schedule_build_striped_blocks(int(seqlen), int(n_ranks), int(stripe), None, 0,
+                                               ctypes.byref(n)), "dfa_schedule_build_striped_blocks")
+    out = np.zeros((n.value, NB), dtype=np.int64)
+    _check(L.dfa_schedule_build_striped_blocks(int(seqlen), int(n_ranks), int(stripe),
+                                               out.ctypes.data_as(ctypes.c_void_p), n.value,
+                                               ctypes.byref(n)), "dfa_schedule_build_striped_blocks")
+    return out
+
+
 def _blocks_arg(blocks) -> np.ndarray:
-    arr = np.ascontiguousarray(np.asarray(blocks, dtype=np.int64).reshape(-1, 10))
-    return arr
+    """[n, 11] int64 dfa_block rows; rows without the trailing run field (10
+    columns) get run = 1."""
+    a = np.asarray(blocks, dtype=np.int64)
+    if a.ndim == 1:
+        a = a.reshape(1, -1)
+    if a.shape[-1] == NB - 1:
+        a = np.concatenate([a.reshape(-1, NB - 1), np.ones((a.size // (NB - 1), 1), np.int64)], axis=1)
+    return np.ascontiguousarray(a.reshape(-1, NB))
 
 
 def dfa_schedule_balance(blocks, n_ranks: int) -> dict:
@@ -194,7 +216,7 @@ def _workspace(desc, blocks, op, device, workspace):
 def dfa_attn_block_fwd(q, k, v, block, o_part=None, lse_part=None, scale=None, stream=None):
     """One block's normalised partial: o_part fp32 [B, Hq, len_q, d], lse_part fp32 [B, Hq, len_q]."""
     import torch
-    blk = DfaBlock(*[int(x) for x in np.asarray(block, dtype=np.int64).reshape(10)])
+    blk = DfaBlock(*[int(x) for x in _blocks_arg(block)[0]])
     desc = make_desc(q, k, v, scale=scale)
     B, _, Hq, D = q.shape
     if o_part is None:

@@ -3,10 +3,10 @@
 // launches on the caller's stream.
 //
 // Planning.  A block list is regrouped two ways:
-//  * by query piece (q_start, len_q, stride): each piece keeps its blocks in
+//  * by query piece (q_start, len_q, stride, run): each piece keeps its blocks in
 //    ring-step order -- the order in which a virtual rank receives key/value
 //    shards -- and is cut into query tiles (forward, dQ);
-//  * by key piece (kv_start, len_kv, stride): each keeps the blocks that read
+//  * by key piece (kv_start, len_kv, stride, run): each keeps the blocks that read
 //    it, again in step order, cut into key tiles (dK, dV).
 // Work tiles are sorted by decreasing cost so the heaviest start first.  The
 // tables travel to the device in the caller's workspace; the kernels read
@@ -67,16 +67,33 @@ bool ptr_aligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) =
 
 dfa_status check_block(const dfa_attn_desc *d, const dfa_block &b) {
   const int64_t N = d->seqlen;
-  if (b.len_q < 1 || b.len_kv < 1 || b.stride < 1) return DFA_E_SHAPE;
+  if (b.len_q < 1 || b.len_kv < 1 || b.stride < 1 || b.run < 1) return DFA_E_SHAPE;
   if (b.q_start < 0 || b.kv_start < 0) return DFA_E_SHAPE;
-  if (b.q_start > N - 1 || (b.len_q - 1) > (N - 1 - b.q_start) / b.stride) return DFA_E_SHAPE;
-  if (b.kv_start > N - 1 || (b.len_kv - 1) > (N - 1 - b.kv_start) / b.stride) return DFA_E_SHAPE;
-  // the block's mask must be the global-position rule
+  if (b.run > 1) {
+    // whole runs that never overlap; the row tiles (64 rows) must not
+    // straddle a run
+    if (b.stride < b.run || b.len_q % b.run || b.len_kv % b.run) return DFA_E_SHAPE;
+    if (b.run % 64) return DFA_E_UNSUPPORTED;
+  }
+  const int64_t rq = (b.len_q - 1) / b.run, rk = (b.len_kv - 1) / b.run;  // last run index
+  if (b.q_start > N - 1 || rq > (N - 1 - b.q_start) / b.stride ||
+      dfa::piece_pos(b.q_start, b.stride, b.run, b.len_q - 1) > N - 1)
+    return DFA_E_SHAPE;
+  if (b.kv_start > N - 1 || rk > (N - 1 - b.kv_start) / b.stride ||
+      dfa::piece_pos(b.kv_start, b.stride, b.run, b.len_kv - 1) > N - 1)
+    return DFA_E_SHAPE;
+  // the block's run-level offset (for run = 1 the exact mask rule)
   if (b.diag_offset != floor_div(b.q_start - b.kv_start, b.stride)) return DFA_E_SHAPE;
   return DFA_OK;
 }
 
-using PieceKey = std::tuple<int64_t, int64_t, int64_t>;  // start, len, stride
+bool any_runs(const dfa_block *blocks, int64_t n) {
+  for (int64_t i = 0; i < n; ++i)
+    if (blocks[i].run > 1) return true;
+  return false;
+}
+
+using PieceKey = std::tuple<int64_t, int64_t, int64_t, int64_t>;  // start, len, stride, run
 
 // Distinct pieces must not share rows.  Returns false on overlap; sets
 // `full` when the pieces cover every position.
@@ -84,9 +101,9 @@ bool pieces_disjoint(const std::vector<PieceKey> &pieces, int64_t N, bool &full)
   std::vector<uint8_t> seen(static_cast<size_t>(N), 0);
   int64_t covered = 0;
   for (const auto &p : pieces) {
-    const int64_t s = std::get<0>(p), len = std::get<1>(p), st = std::get<2>(p);
+    const int64_t s = std::get<0>(p), len = std::get<1>(p), st = std::get<2>(p), run = std::get<3>(p);
     for (int64_t i = 0; i < len; ++i) {
-      uint8_t &x = seen[static_cast<size_t>(s + i * st)];
+      uint8_t &x = seen[static_cast<size_t>(dfa::piece_pos(s, st, run, i))];
       if (x) return false;
       x = 1;
     }
@@ -110,7 +127,7 @@ dfa_status plan_q(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n, in
   std::vector<PieceKey> order;
   for (int64_t i = 0; i < n; ++i) {
     const dfa_block &b = blocks[i];
-    PieceKey key{b.q_start, b.len_q, b.stride};
+    PieceKey key{b.q_start, b.len_q, b.stride, b.run};
     auto it = by_piece.find(key);
     if (it == by_piece.end()) {
       order.push_back(key);
@@ -135,22 +152,23 @@ dfa_status plan_q(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n, in
     s.q_start = std::get<0>(key);
     s.len_q = std::get<1>(key);
     s.stride = std::get<2>(key);
+    s.run = std::get<3>(key);
     s.part_off = 0;
     s.blk_begin = static_cast<int32_t>(out.kv.size());
     s.blk_count = static_cast<int32_t>(idx.size());
-    for (int64_t bi : idx) {
-      if (blocks[bi].stride != s.stride) return DFA_E_SHAPE;
+    for (int64_t bi : idx)
       out.kv.push_back(KvRef{blocks[bi].kv_start, blocks[bi].len_kv, blocks[bi].diag_offset});
-    }
     const int32_t seg_id = static_cast<int32_t>(out.segs.size());
     out.segs.push_back(s);
     const int64_t nt = ceil_div(s.len_q, tileq);
     for (int64_t t = 0; t < nt; ++t) {
       const int64_t iend = std::min<int64_t>((t + 1) * tileq, s.len_q);
+      const int64_t q_last = dfa::piece_pos(s.q_start, s.stride, s.run, iend - 1);
       int64_t c = 0;
       for (int64_t bi : idx) {
-        const int64_t hi = std::min<int64_t>(blocks[bi].len_kv, iend + blocks[bi].diag_offset);
-        if (hi > 0) c += ceil_div(hi, kCostTileKV);
+        const int64_t hi = dfa::piece_count_le(blocks[bi].kv_start, s.stride, s.run,
+                                               blocks[bi].len_kv, q_last);
+        c += ceil_div(hi, kCostTileKV);
       }
       costs.push_back(Cost{c, Tile{seg_id, static_cast<int32_t>(t)}});
     }
@@ -176,7 +194,7 @@ dfa_status plan_kv(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n, i
   std::vector<PieceKey> order;
   for (int64_t i = 0; i < n; ++i) {
     const dfa_block &b = blocks[i];
-    PieceKey key{b.kv_start, b.len_kv, b.stride};
+    PieceKey key{b.kv_start, b.len_kv, b.stride, b.run};
     auto it = by_piece.find(key);
     if (it == by_piece.end()) {
       order.push_back(key);
@@ -201,21 +219,21 @@ dfa_status plan_kv(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n, i
     s.kv_start = std::get<0>(key);
     s.len_kv = std::get<1>(key);
     s.stride = std::get<2>(key);
+    s.run = std::get<3>(key);
     s.blk_begin = static_cast<int32_t>(out.q.size());
     s.blk_count = static_cast<int32_t>(idx.size());
-    for (int64_t bi : idx) {
-      if (blocks[bi].stride != s.stride) return DFA_E_SHAPE;
+    for (int64_t bi : idx)
       out.q.push_back(QRef{blocks[bi].q_start, blocks[bi].len_q, blocks[bi].diag_offset});
-    }
     const int32_t seg_id = static_cast<int32_t>(out.segs.size());
     out.segs.push_back(s);
     const int64_t nt = ceil_div(s.len_kv, tilek);
     for (int64_t t = 0; t < nt; ++t) {
-      const int64_t j0 = t * tilek;
+      const int64_t gk0 = dfa::piece_pos(s.kv_start, s.stride, s.run, t * tilek);
       int64_t c = 0;
       for (int64_t bi : idx) {
-        // query rows i >= j0 - diag see at least one key of the tile
-        const int64_t lo = std::max<int64_t>(0, j0 - blocks[bi].diag_offset);
+        // query rows at or after the tile's first key see at least one key
+        const int64_t lo = dfa::piece_count_le(blocks[bi].q_start, s.stride, s.run,
+                                               blocks[bi].len_q, gk0 - 1);
         if (lo < blocks[bi].len_q) c += ceil_div(blocks[bi].len_q - lo, kCostTileKV);
       }
       costs.push_back(Cost{c, Tile{seg_id, static_cast<int32_t>(t)}});
@@ -309,7 +327,7 @@ void plan_steps(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n, int 
     std::vector<std::vector<PieceKey>> used;
     for (size_t p = pos; p < end; ++p) {
       const dfa_block &b = blocks[idx[p]];
-      PieceKey key{b.q_start, b.len_q, b.stride};
+      PieceKey key{b.q_start, b.len_q, b.stride, b.run};
       size_t r = 0;
       while (r < rounds.size() &&
              std::find(used[r].begin(), used[r].end(), key) != used[r].end())
@@ -330,6 +348,7 @@ void plan_steps(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n, int 
         s.q_start = b.q_start;
         s.len_q = b.len_q;
         s.stride = b.stride;
+        s.run = b.run;
         s.part_off = R.part_rows;
         s.blk_begin = static_cast<int32_t>(sp.kv.size());
         s.blk_count = 1;
@@ -338,7 +357,7 @@ void plan_steps(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n, int 
         sp.segs.push_back(s);
         const int64_t nt = ceil_div(b.len_q, tileq);
         for (int64_t t = 0; t < nt; ++t) sp.tiles.push_back(Tile{sid, static_cast<int32_t>(t)});
-        sp.items.push_back(MergeItem{b.q_start, b.len_q, b.stride, R.part_rows});
+        sp.items.push_back(MergeItem{b.q_start, b.len_q, b.stride, b.run, R.part_rows});
         R.part_rows += BH * b.len_q;
         R.max_len = std::max<int64_t>(R.max_len, b.len_q);
       }
@@ -492,7 +511,8 @@ extern "C" dfa_status dfa_attn_block_fwd(const dfa_attn_desc *d, const dfa_block
   a.o = o_part;
   a.lse = lse_part;
   a.out_mode = 1;
-  a.seg0 = QSeg{blk->q_start, blk->len_q, blk->stride, 0, 0, 1};
+  a.runs = blk->run > 1;
+  a.seg0 = QSeg{blk->q_start, blk->len_q, blk->stride, blk->run, 0, 0, 1};
   a.kv0 = KvRef{blk->kv_start, blk->len_kv, blk->diag_offset};
   const int tq = fwd_tile(d);
   const int64_t grid = ceil_div(blk->len_q, tq) * d->batch * d->heads_q;
@@ -530,6 +550,7 @@ extern "C" dfa_status dfa_attn_fwd(const dfa_attn_desc *d, const dfa_block *bloc
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int hd = d->head_dim;
   dfa::FwdArgs a{};
+  a.runs = any_runs(blocks, n_blocks);
   a.g = make_geom(d);
   a.q = q;
   a.k = k;
@@ -636,7 +657,8 @@ extern "C" dfa_status dfa_attn_bwd_ex(const dfa_attn_desc *d, const dfa_block *b
     const int64_t row_bytes = 2 * std::max(std::max(d->q_strides[1], d->o_strides[1]),
                                            std::max(d->k_strides[1], d->v_strides[1]));
     for (int64_t i = 0; i < n_blocks; ++i)
-      if (row_bytes * blocks[i].stride >= (int64_t{1} << 31) / 64) return DFA_E_UNSUPPORTED;
+      if (row_bytes * dfa::piece_row_step(blocks[i].stride, blocks[i].run) >= (int64_t{1} << 31) / 64)
+        return DFA_E_UNSUPPORTED;
   }
   QPlan qp;
   KvPlan kp;
@@ -674,6 +696,7 @@ extern "C" dfa_status dfa_attn_bwd_ex(const dfa_attn_desc *d, const dfa_block *b
   if (st != DFA_OK) return st;
   char *ws = static_cast<char *>(workspace);
   dfa::BwdArgs a{};
+  a.runs = any_runs(blocks, n_blocks);
   a.g = make_geom(d);
   a.q = q;
   a.k = k;

@@ -34,7 +34,9 @@ constexpr int DQ_BQ = kDqTileQ;  // 32 query rows per wave
 constexpr int DQ_BK = 64;
 static_assert(DQ_BQ == 32 * NW, "one 32-query column block per wave");
 
-template <int HD>
+// RUNS: pieces made of runs (stripe blocks), visibility from global
+// positions; otherwise rows start + i*stride and each block's diagonal.
+template <int HD, bool RUNS>
 __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
   using TL = Tile64<HD>;
   static_assert(TL::ROWS == DQ_BK, "key tiles are 64 rows");
@@ -56,6 +58,12 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
   const int64_t i0 = static_cast<int64_t>(tl.tile) * DQ_BQ;
   const int64_t i0w = i0 + wave * 32;
   const int64_t iend = (i0 + DQ_BQ < seg.len_q) ? i0 + DQ_BQ : seg.len_q;
+  auto pos_of = [&](int64_t start, int64_t i) {
+    return RUNS ? piece_pos(start, seg.stride, seg.run, i) : start + i * seg.stride;
+  };
+  const int64_t rs = RUNS ? piece_row_step(seg.stride, seg.run) : seg.stride;  // row step in a tile
+  const int64_t q_last = RUNS ? pos_of(seg.q_start, iend - 1) : 0;
+  const int64_t gq_w = RUNS ? pos_of(seg.q_start, i0w) : 0;
 
   const char *kb = static_cast<const char *>(a.k) + 2 * (b * G.ks[0] + hk * G.ks[2]);
   const char *vb = static_cast<const char *>(a.v) + 2 * (b * G.vs[0] + hk * G.vs[2]);
@@ -64,13 +72,16 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
   struct Walk {
     int64_t kv_start, len_kv, diag, ntiles;
   };
-  auto walk = [&](int k) {
+  auto walk = [&](int k) {  // key tiles holding a key at or before the last row
     const KvRef r = ld_table(a.qkv + seg.blk_begin + k);
-    Walk w{r.kv_start, r.len_kv, r.diag_offset, 0};
-    int64_t hi = iend + r.diag_offset;
-    if (hi > r.len_kv) hi = r.len_kv;
-    w.ntiles = hi > 0 ? (hi + DQ_BK - 1) / DQ_BK : 0;
-    return w;
+    int64_t hi;
+    if constexpr (RUNS) {
+      hi = piece_count_le(r.kv_start, seg.stride, seg.run, r.len_kv, q_last);
+    } else {
+      hi = iend + r.diag_offset;
+      if (hi > r.len_kv) hi = r.len_kv;
+    }
+    return Walk{r.kv_start, r.len_kv, r.diag_offset, hi > 0 ? (hi + DQ_BK - 1) / DQ_BK : 0};
   };
   const int nblk = seg.blk_count;
   auto first = [&](int &k_, Walk &w_) {
@@ -92,7 +103,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
   first(k, cw);
 
   // K and V stream
-  const TileStream<HD, NW> ld(wave, lane, 2 * G.ks[1] * seg.stride, 2 * G.vs[1] * seg.stride);
+  const TileStream<HD, NW> ld(wave, lane, 2 * G.ks[1] * rs, 2 * G.vs[1] * rs);
   const int per_tile = 2 * ld.count();
   const unsigned lds0 = lds_addr(smem);
   int kl = k;
@@ -101,7 +112,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
   int issued = 0;
   auto issue = [&](int stage) {
     const int64_t jt = tl_ * DQ_BK;
-    const int64_t p0 = lw.kv_start + jt * seg.stride;
+    const int64_t p0 = pos_of(lw.kv_start, jt);
     ld.load(kb + 2 * p0 * G.ks[1], vb + 2 * p0 * G.vs[1], lds0 + stage * STAGE,
             lds0 + stage * STAGE + TB, lw.len_kv - jt);
     ++issued;
@@ -115,7 +126,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
   bf16x8 qf[KS], df[KS];
   const int64_t row = i0w + c32;
   const bool valid = row < seg.len_q;
-  const int64_t pos = seg.q_start + (valid ? row : seg.len_q - 1) * seg.stride;
+  const int64_t pos = pos_of(seg.q_start, valid ? row : seg.len_q - 1);
   {
     const char *qsrc = static_cast<const char *>(a.q) + 2 * (b * G.qs[0] + pos * G.qs[1] + h * G.qs[2]);
     const char *dsrc = static_cast<const char *>(a.dout) + 2 * (b * G.os[0] + pos * G.os[1] + h * G.os[2]);
@@ -145,15 +156,23 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
     if (kl < nblk) issue((it + NS - 1) % NS);
 
     const int64_t j0 = t * DQ_BK;
-    if (j0 <= i0w + 31 + cw.diag) {
+    // this wave's row ii sees the tile's key jj iff jj <= ii + dw
+    int64_t dw;
+    if constexpr (RUNS) {
+      const int64_t gk = pos_of(cw.kv_start, j0);
+      dw = rs == 1 ? gq_w - gk : floor_div64(gq_w - gk, rs);
+    } else {
+      dw = i0w + cw.diag - j0;
+    }
+    if (dw + 31 >= 0) {
       const char *kt = smem + (it % NS) * STAGE;
       const char *vt = kt + TB;
-      const bool need_mask = (j0 + DQ_BK - 1 > i0w + cw.diag) || (j0 + DQ_BK > cw.len_kv);
+      const bool need_mask = (dw < DQ_BK - 1) || (j0 + DQ_BK > cw.len_kv);
       int x = 0;
       if (need_mask) {
         // element i of half kh is local key jj = 32kh + 16(i/8) + 8g + i%8,
         // visible iff jj <= lim; x = 8g - lim
-        const int64_t lim64 = row + cw.diag - j0, len64 = cw.len_kv - 1 - j0;
+        const int64_t lim64 = c32 + dw, len64 = cw.len_kv - 1 - j0;
         const int64_t m64 = lim64 < len64 ? lim64 : len64;
         x = 8 * g - static_cast<int>(m64 < -1 ? -1 : (m64 > DQ_BK ? DQ_BK : m64));
       }
@@ -219,7 +238,7 @@ static_assert(KV_BK == 32 * NW, "one 32-key column block per wave");
 // SIMD and hide each other's LDS and exponent latency; S is recomputed in both.
 constexpr int KV_DV = 1, KV_DK = 2;
 
-template <int HD, int MODE>
+template <int HD, int MODE, bool RUNS>
 __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
   using TL = Tile64<HD>;
   static_assert(TL::ROWS == KV_BQ, "query tiles are 64 rows");
@@ -245,7 +264,14 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
   const int64_t j0w = j0 + wave * 32;
   const int64_t col = j0w + c32;  // this lane's key row
   const bool valid = col < seg.len_kv;
-  const int64_t pos = seg.kv_start + (valid ? col : seg.len_kv - 1) * seg.stride;
+  auto pos_of = [&](int64_t start, int64_t i) {
+    return RUNS ? piece_pos(start, seg.stride, seg.run, i) : start + i * seg.stride;
+  };
+  const int64_t pos = pos_of(seg.kv_start, valid ? col : seg.len_kv - 1);
+  const int64_t rs = RUNS ? piece_row_step(seg.stride, seg.run) : seg.stride;  // row step in a tile
+  // global positions of the workgroup's and this wave's first key
+  const int64_t gk0 = RUNS ? pos_of(seg.kv_start, j0) : 0;
+  const int64_t gk_w = RUNS ? pos_of(seg.kv_start, j0w) : 0;
 
   // walk over (group head, block, query tile)
   struct Walk {
@@ -255,8 +281,14 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
   auto walk = [&](int gi, int k) {
     const QRef r = ld_table(a.kvq + seg.blk_begin + k);
     Walk w{r.q_start, r.len_q, r.diag_offset, 0, 0, hk * G.group + gi};
-    int64_t lo = j0 - r.diag_offset;  // first query row that sees key row j0
-    if (lo < 0) lo = 0;
+    // the first query row at or after the workgroup's first key
+    int64_t lo;
+    if constexpr (RUNS) {
+      lo = piece_count_le(r.q_start, seg.stride, seg.run, r.len_q, gk0 - 1);
+    } else {
+      lo = j0 - r.diag_offset;
+      if (lo < 0) lo = 0;
+    }
     if (lo < r.len_q) {
       w.t0 = lo / KV_BQ;
       w.t1 = (r.len_q + KV_BQ - 1) / KV_BQ;
@@ -289,7 +321,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
   // Q/dO stream; LSE*log2(e) and D of the 64 rows go to LDS with one 4-byte
   // direct load each, issued by the last two waves (they have the fewest
   // tile instructions)
-  const TileStream<HD, NW> ld(wave, lane, 2 * G.qs[1] * seg.stride, 2 * G.os[1] * seg.stride);
+  const TileStream<HD, NW> ld(wave, lane, 2 * G.qs[1] * rs, 2 * G.os[1] * rs);
   const bool stats_wave = wave >= NW - 2;
   const int per_tile = 2 * ld.count() + (stats_wave ? 1 : 0);
   const unsigned lds0 = lds_addr(smem);
@@ -299,7 +331,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
   int issued = 0;
   auto issue = [&](int stage) {
     const int64_t i0 = tl_ * KV_BQ;
-    const int64_t p0 = lw.q_start + i0 * seg.stride;
+    const int64_t p0 = pos_of(lw.q_start, i0);
     const char *qb = static_cast<const char *>(a.q) + 2 * (b * G.qs[0] + p0 * G.qs[1] + lw.h * G.qs[2]);
     const char *db = static_cast<const char *>(a.dout) + 2 * (b * G.os[0] + p0 * G.os[1] + lw.h * G.os[2]);
     const unsigned sb = lds0 + stage * STAGE;
@@ -309,7 +341,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
       const unsigned r = static_cast<unsigned>(lane < rows ? lane : rows - 1);
       const int64_t row0 = (static_cast<int64_t>(b) * G.hq + lw.h) * G.seqlen + p0;
       const float *src = wave == NW - 2 ? a.lse2 : a.dd;
-      dma4(src + row0, r * static_cast<unsigned>(seg.stride) * 4u,
+      dma4(src + row0, r * static_cast<unsigned>(rs) * 4u,
            sb + 2 * TB + (wave == NW - 2 ? 0 : KV_BQ * 4));
     }
     ++issued;
@@ -347,17 +379,25 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
     if (gl < ngrp) issue((it + NS - 1) % NS);
 
     const int64_t qi0 = t * KV_BQ;
+    // query row qq of the tile sees this wave's key c32 iff c32 <= qq + dw
+    int64_t dw;
+    if constexpr (RUNS) {
+      const int64_t gq = pos_of(cw.q_start, qi0);
+      dw = rs == 1 ? gq - gk_w : floor_div64(gq - gk_w, rs);
+    } else {
+      dw = qi0 + cw.diag - j0w;
+    }
     // some pair of this wave visible: largest query row sees smallest key row
-    if (qi0 + KV_BQ - 1 + cw.diag >= j0w) {
+    if (KV_BQ - 1 + dw >= 0) {
       const char *qt = smem + (it % NS) * STAGE;
       const char *dt_ = qt + TB;
       const float *lt = reinterpret_cast<const float *>(qt + 2 * TB);
       const float *ddt = lt + KV_BQ;
       // local query qq (0..63) of the tile is kept iff lo <= qq < hi
-      const bool need_mask = (qi0 + cw.diag < j0w + 31) || (qi0 + KV_BQ > cw.len_q);
+      const bool need_mask = (dw < 31) || (qi0 + KV_BQ > cw.len_q);
       int lo = 0, hi = KV_BQ;
       if (need_mask) {
-        const int64_t lo64 = col - cw.diag - qi0, hi64 = cw.len_q - qi0;
+        const int64_t lo64 = c32 - dw, hi64 = cw.len_q - qi0;
         lo = static_cast<int>(lo64 < 0 ? 0 : (lo64 > KV_BQ ? KV_BQ : lo64));
         hi = static_cast<int>(hi64 > KV_BQ ? KV_BQ : hi64);
       }
@@ -435,31 +475,47 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
 hipError_t launch_bwd_dq_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (hd == 128)
-    hipLaunchKernelGGL(dq_bf16_kernel<128>, dim3(static_cast<unsigned>(grid)), dim3(NT), 0, s, a);
-  else if (hd == 64)
-    hipLaunchKernelGGL(dq_bf16_kernel<64>, dim3(static_cast<unsigned>(grid)), dim3(NT), 0, s, a);
-  else
+  const dim3 gr(static_cast<unsigned>(grid)), bl(NT);
+  if (hd == 128) {
+    if (a.runs)
+      hipLaunchKernelGGL((dq_bf16_kernel<128, true>), gr, bl, 0, s, a);
+    else
+      hipLaunchKernelGGL((dq_bf16_kernel<128, false>), gr, bl, 0, s, a);
+  } else if (hd == 64) {
+    if (a.runs)
+      hipLaunchKernelGGL((dq_bf16_kernel<64, true>), gr, bl, 0, s, a);
+    else
+      hipLaunchKernelGGL((dq_bf16_kernel<64, false>), gr, bl, 0, s, a);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
+}
+
+template <int HD, int MODE>
+void launch_dkdv_variant(const BwdArgs &a, dim3 gr, hipStream_t s) {
+  if (a.runs)
+    hipLaunchKernelGGL((dkdv_bf16_kernel<HD, MODE, true>), gr, dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((dkdv_bf16_kernel<HD, MODE, false>), gr, dim3(NT), 0, s, a);
 }
 
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs &a, int hd, int64_t grid, int which, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (which != KV_DK && which != KV_DV) return hipErrorInvalidValue;
-  const dim3 gr(static_cast<unsigned>(grid)), bl(NT);
+  const dim3 gr(static_cast<unsigned>(grid));
   const bool dk = which == KV_DK;
   if (hd == 128) {
     if (dk)
-      hipLaunchKernelGGL((dkdv_bf16_kernel<128, KV_DK>), gr, bl, 0, s, a);
+      launch_dkdv_variant<128, KV_DK>(a, gr, s);
     else
-      hipLaunchKernelGGL((dkdv_bf16_kernel<128, KV_DV>), gr, bl, 0, s, a);
+      launch_dkdv_variant<128, KV_DV>(a, gr, s);
   } else if (hd == 64) {
     if (dk)
-      hipLaunchKernelGGL((dkdv_bf16_kernel<64, KV_DK>), gr, bl, 0, s, a);
+      launch_dkdv_variant<64, KV_DK>(a, gr, s);
     else
-      hipLaunchKernelGGL((dkdv_bf16_kernel<64, KV_DV>), gr, bl, 0, s, a);
+      launch_dkdv_variant<64, KV_DV>(a, gr, s);
   } else {
     return hipErrorInvalidValue;
   }

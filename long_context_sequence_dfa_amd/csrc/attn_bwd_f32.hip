@@ -42,7 +42,7 @@ __global__ __launch_bounds__(TQ) void dq_f32_kernel(BwdArgs a) {
   float lse = 0.f, dd = 0.f;
   int64_t pos = 0;
   if (valid) {
-    pos = seg.q_start + row * seg.stride;
+    pos = piece_pos(seg.q_start, seg.stride, seg.run, row);
 #pragma unroll
     for (int c = 0; c < HD; ++c) {
       qv[c] = qp[pos * G.qs[1] + c];
@@ -58,8 +58,9 @@ __global__ __launch_bounds__(TQ) void dq_f32_kernel(BwdArgs a) {
   for (int c = 0; c < HD; ++c) acc[c] = 0.f;
   for (int k = 0; k < seg.blk_count; ++k) {
     const KvRef r = a.qkv[seg.blk_begin + k];
-    int64_t hi = rlast + 1 + r.diag_offset;
-    if (hi > r.len_kv) hi = r.len_kv;
+    // keys at or before the tile's last query row
+    const int64_t hi = piece_count_le(r.kv_start, seg.stride, seg.run, r.len_kv,
+                                      piece_pos(seg.q_start, seg.stride, seg.run, rlast));
     for (int64_t j0 = 0; j0 < hi; j0 += TS) {
       __syncthreads();
       for (int e = tid; e < TS * HD; e += TQ) {
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(TQ) void dq_f32_kernel(BwdArgs a) {
         const int64_t j = j0 + jj;
         float x = 0.f, y = 0.f;
         if (j < r.len_kv) {
-          const int64_t kpos = r.kv_start + j * seg.stride;
+          const int64_t kpos = piece_pos(r.kv_start, seg.stride, seg.run, j);
           x = kp[kpos * G.ks[1] + c];
           y = vp[kpos * G.vs[1] + c];
         }
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(TQ) void dq_f32_kernel(BwdArgs a) {
       if (!valid) continue;
       for (int jj = 0; jj < TS; ++jj) {
         const int64_t j = j0 + jj;
-        if (j >= r.len_kv || j > row + r.diag_offset) continue;
+        if (j >= r.len_kv || piece_pos(r.kv_start, seg.stride, seg.run, j) > pos) continue;
         float s = 0.f, dp = 0.f;
 #pragma unroll
         for (int c = 0; c < HD; ++c) {
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(TK) void dkdv_f32_kernel(BwdArgs a) {
   float kv_[HD], vv[HD], dk[HD], dv[HD];
   int64_t pos = 0;
   if (valid) {
-    pos = seg.kv_start + j * seg.stride;
+    pos = piece_pos(seg.kv_start, seg.stride, seg.run, j);
 #pragma unroll
     for (int c = 0; c < HD; ++c) {
       kv_[c] = kp[pos * G.ks[1] + c];
@@ -139,8 +140,9 @@ __global__ __launch_bounds__(TK) void dkdv_f32_kernel(BwdArgs a) {
     const float *ddp = a.dd + (static_cast<int64_t>(b) * G.hq + h) * G.seqlen;
     for (int k = 0; k < seg.blk_count; ++k) {
       const QRef r = a.kvq[seg.blk_begin + k];
-      int64_t lo = j0 - r.diag_offset;  // first query row that sees key row j0
-      if (lo < 0) lo = 0;
+      // the first query row at or after the tile's first key
+      const int64_t lo = piece_count_le(r.q_start, seg.stride, seg.run, r.len_q,
+                                        piece_pos(seg.kv_start, seg.stride, seg.run, j0) - 1);
       for (int64_t i0 = lo; i0 < r.len_q; i0 += TS) {
         __syncthreads();
         for (int e = tid; e < TS * HD; e += TK) {
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(TK) void dkdv_f32_kernel(BwdArgs a) {
           const int64_t i = i0 + ii;
           float x = 0.f, y = 0.f;
           if (i < r.len_q) {
-            const int64_t qpos = r.q_start + i * seg.stride;
+            const int64_t qpos = piece_pos(r.q_start, seg.stride, seg.run, i);
             x = qp[qpos * G.qs[1] + c];
             y = dop[qpos * G.os[1] + c];
           }
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(TK) void dkdv_f32_kernel(BwdArgs a) {
         }
         if (tid < TS) {
           const int64_t i = i0 + tid;
-          const int64_t qpos = r.q_start + i * seg.stride;
+          const int64_t qpos = piece_pos(r.q_start, seg.stride, seg.run, i < r.len_q ? i : 0);
           ls_[tid] = i < r.len_q ? lsep[qpos] : 0.f;
           dd_[tid] = i < r.len_q ? ddp[qpos] : 0.f;
         }
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(TK) void dkdv_f32_kernel(BwdArgs a) {
         if (!valid) continue;
         for (int ii = 0; ii < TS; ++ii) {
           const int64_t i = i0 + ii;
-          if (i >= r.len_q || j > i + r.diag_offset) continue;
+          if (i >= r.len_q || pos > piece_pos(r.q_start, seg.stride, seg.run, i)) continue;
           float s = 0.f, dp = 0.f;
 #pragma unroll
           for (int c = 0; c < HD; ++c) {

@@ -49,9 +49,13 @@ struct BlockWalk {
   int64_t kv_start, len_kv, diag, ntiles;
 };
 
-template <bool TABLE>
+// The key piece of block k; ntiles covers every key at or before the
+// workgroup's last query row (local row iend-1, global position q_last).
+// RUNS: pieces made of runs (stripe blocks), visibility from global
+// positions; otherwise rows start + i*stride and the block's diagonal.
+template <bool TABLE, bool RUNS>
 __device__ __forceinline__ BlockWalk block_walk(const FwdArgs &a, const QSeg &seg, int k,
-                                                int64_t iend) {
+                                                int64_t iend, int64_t q_last) {
   KvRef r;
   if constexpr (TABLE)
     r = ld_table(a.kv + seg.blk_begin + k);
@@ -61,16 +65,20 @@ __device__ __forceinline__ BlockWalk block_walk(const FwdArgs &a, const QSeg &se
   w.kv_start = r.kv_start;
   w.len_kv = r.len_kv;
   w.diag = r.diag_offset;
-  // the last row iend-1 sees keys j <= iend-1+diag
-  int64_t hi = iend + r.diag_offset;
-  if (hi > r.len_kv) hi = r.len_kv;
+  int64_t hi;
+  if constexpr (RUNS) {
+    hi = piece_count_le(r.kv_start, seg.stride, seg.run, r.len_kv, q_last);
+  } else {
+    hi = iend + r.diag_offset;  // the last row iend-1 sees keys j <= iend-1+diag
+    if (hi > r.len_kv) hi = r.len_kv;
+  }
   w.ntiles = hi > 0 ? (hi + BK - 1) / BK : 0;
   return w;
 }
 
 // TABLE: the query piece and its blocks come from the work tables (fused and
 // stepwise walks); otherwise from seg0/kv0 (one block).
-template <int HD, int OUT, bool TABLE>
+template <int HD, int OUT, bool TABLE, bool RUNS>
 __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   using TL = Tile64<HD>;
   static_assert(TL::ROWS == BK, "key tiles are 64 rows");
@@ -104,6 +112,15 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   const int64_t i0 = qt * BQ;
   const int64_t i0w = i0 + wave * 32;
   const int64_t iend = (i0 + BQ < seg.len_q) ? i0 + BQ : seg.len_q;
+  // global position of local row i of a piece of this workgroup
+  auto pos_of = [&](int64_t start, int64_t i) {
+    return RUNS ? piece_pos(start, seg.stride, seg.run, i) : start + i * seg.stride;
+  };
+  const int64_t rs = RUNS ? piece_row_step(seg.stride, seg.run) : seg.stride;  // row step in a tile
+  const int64_t q_last = RUNS ? pos_of(seg.q_start, iend - 1) : 0;
+  // global position of this wave's first row (extrapolated past a ragged end:
+  // only the mask's row comparisons use it)
+  const int64_t gq_w = RUNS ? pos_of(seg.q_start, i0w) : 0;
   const float c = G.scale_log2;
 
   const char *qb = static_cast<const char *>(a.q) + 2 * (b * G.qs[0] + h * G.qs[2]);
@@ -116,7 +133,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   {
     int64_t row = i0w + c32;
     row = row < seg.len_q ? row : seg.len_q - 1;
-    const char *src = qb + 2 * (seg.q_start + row * seg.stride) * G.qs[1];
+    const char *src = qb + 2 * pos_of(seg.q_start, row) * G.qs[1];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ld16(src + (2 * ks + g) * 16));
   }
@@ -130,7 +147,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   const int nblk = TABLE ? seg.blk_count : 1;
   auto first = [&](int &k_, BlockWalk &w_) {
     while (k_ < nblk) {
-      w_ = block_walk<TABLE>(a, seg, k_, iend);
+      w_ = block_walk<TABLE, RUNS>(a, seg, k_, iend, q_last);
       if (w_.ntiles > 0) return;
       ++k_;
     }
@@ -147,7 +164,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   first(k, cw);
 
   // ---- K/V stream: NS LDS stages, the load cursor runs NS - 1 tiles ahead ----
-  const TileStream<HD, NW> ld(wave, lane, 2 * G.ks[1] * seg.stride, 2 * G.vs[1] * seg.stride);
+  const TileStream<HD, NW> ld(wave, lane, 2 * G.ks[1] * rs, 2 * G.vs[1] * rs);
   const int per_tile = 2 * ld.count();
   const unsigned lds0 = lds_addr(smem);
   int kl = k;
@@ -156,7 +173,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   int issued = 0;
   auto issue = [&](int stage) {
     const int64_t j0 = tl * BK;
-    const int64_t p0 = lw.kv_start + j0 * seg.stride;
+    const int64_t p0 = pos_of(lw.kv_start, j0);
     ld.load(kb + 2 * p0 * G.ks[1], vb + 2 * p0 * G.vs[1], lds0 + stage * STAGE,
             lds0 + stage * STAGE + TB, lw.len_kv - j0);
     ++issued;
@@ -181,7 +198,16 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     if (kl < nblk) issue((it + NS - 1) % NS);
 
     const int64_t j0 = t * BK;
-    if (j0 <= i0w + 31 + cw.diag) {  // some row of this wave sees a key of the tile
+    // this wave's row ii sees the tile's key jj iff jj <= ii + dw (global
+    // positions, in units of the row step)
+    int64_t dw;
+    if constexpr (RUNS) {
+      const int64_t gk = pos_of(cw.kv_start, j0);
+      dw = rs == 1 ? gq_w - gk : floor_div64(gq_w - gk, rs);
+    } else {
+      dw = i0w + cw.diag - j0;
+    }
+    if (dw + 31 >= 0) {  // some row of this wave sees a key of the tile
       const char *kt = smem + (it % NS) * STAGE;
       const char *vt = kt + TB;
       f32x16 s0 = f32x16{}, s1 = f32x16{};
@@ -195,9 +221,9 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
       }
       __builtin_amdgcn_s_setprio(0);
       // element i of s0 / s1 is key j0 + 32*(i/16) + 16*((i%16)/8) + 8g + i%8
-      if ((j0 + BK - 1 > i0w + cw.diag) || (j0 + BK > cw.len_kv)) {
+      if ((dw < BK - 1) || (j0 + BK > cw.len_kv)) {
         // key j0 + jj is visible iff jj <= lim; x = 8g - lim
-        const int64_t lim64 = i0w + c32 + cw.diag - j0;
+        const int64_t lim64 = c32 + dw;
         const int64_t len64 = cw.len_kv - 1 - j0;
         const int64_t m64 = lim64 < len64 ? lim64 : len64;
         const int x = 8 * g - static_cast<int>(m64 < -1 ? -1 : (m64 > BK ? BK : m64));
@@ -261,7 +287,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   const int64_t row = i0w + c32;
   if (row < seg.len_q) {
     if (OUT == 0) {
-      const int64_t pos = seg.q_start + row * seg.stride;
+      const int64_t pos = pos_of(seg.q_start, row);
       char *ob = static_cast<char *>(a.o) + 2 * (b * G.os[0] + pos * G.os[1] + h * G.os[2]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -293,25 +319,32 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
 
 }  // namespace
 
+template <int HD, bool RUNS>
+void launch_fwd_variant(const FwdArgs &a, dim3 gr, hipStream_t s) {
+  const dim3 bl(NT);
+  if (a.out_mode == 0)
+    hipLaunchKernelGGL((fwd_bf16_kernel<HD, 0, true, RUNS>), gr, bl, 0, s, a);
+  else if (a.segs)
+    hipLaunchKernelGGL((fwd_bf16_kernel<HD, 1, true, RUNS>), gr, bl, 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<HD, 1, false, RUNS>), gr, bl, 0, s, a);
+}
+
 hipError_t launch_fwd_bf16(const FwdArgs &a, int hd, int64_t grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.out_mode == 0 && !a.segs) return hipErrorInvalidValue;
-  const dim3 gr(static_cast<unsigned>(grid)), bl(NT);
+  const dim3 gr(static_cast<unsigned>(grid));
   if (hd == 128) {
-    if (a.out_mode == 0)
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, 0, true>), gr, bl, 0, s, a);
-    else if (a.segs)
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, 1, true>), gr, bl, 0, s, a);
+    if (a.runs)
+      launch_fwd_variant<128, true>(a, gr, s);
     else
-      hipLaunchKernelGGL((fwd_bf16_kernel<128, 1, false>), gr, bl, 0, s, a);
+      launch_fwd_variant<128, false>(a, gr, s);
   } else if (hd == 64) {
-    if (a.out_mode == 0)
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, 0, true>), gr, bl, 0, s, a);
-    else if (a.segs)
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, 1, true>), gr, bl, 0, s, a);
+    if (a.runs)
+      launch_fwd_variant<64, true>(a, gr, s);
     else
-      hipLaunchKernelGGL((fwd_bf16_kernel<64, 1, false>), gr, bl, 0, s, a);
+      launch_fwd_variant<64, false>(a, gr, s);
   } else {
     return hipErrorInvalidValue;
   }

@@ -40,6 +40,7 @@ __global__ __launch_bounds__(TQ) void fwd_f32_kernel(FwdArgs a) {
   const int64_t row = qt * TQ + tid;
   const bool valid = row < seg.len_q;
   const int64_t rlast = ((qt + 1) * TQ < seg.len_q ? (qt + 1) * TQ : seg.len_q) - 1;
+  const int64_t qpos = piece_pos(seg.q_start, seg.stride, seg.run, valid ? row : rlast);
 
   const float *qp = static_cast<const float *>(a.q) + b * G.qs[0] + h * G.qs[2];
   const float *kp = static_cast<const float *>(a.k) + b * G.ks[0] + hk * G.ks[2];
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(TQ) void fwd_f32_kernel(FwdArgs a) {
 
   float qv[HD], acc[HD];
   if (valid) {
-    const float *src = qp + (seg.q_start + row * seg.stride) * G.qs[1];
+    const float *src = qp + piece_pos(seg.q_start, seg.stride, seg.run, row) * G.qs[1];
 #pragma unroll
     for (int c = 0; c < HD; ++c) qv[c] = src[c];
   } else {
@@ -61,8 +62,9 @@ __global__ __launch_bounds__(TQ) void fwd_f32_kernel(FwdArgs a) {
   const int nblk = a.segs ? seg.blk_count : 1;
   for (int k = 0; k < nblk; ++k) {
     const KvRef r = a.segs ? a.kv[seg.blk_begin + k] : a.kv0;
-    int64_t hi = rlast + 1 + r.diag_offset;  // keys any row of the tile may see
-    if (hi > r.len_kv) hi = r.len_kv;
+    // keys at or before the tile's last query row
+    const int64_t hi = piece_count_le(r.kv_start, seg.stride, seg.run, r.len_kv,
+                                      piece_pos(seg.q_start, seg.stride, seg.run, rlast));
     for (int64_t j0 = 0; j0 < hi; j0 += TK) {
       __syncthreads();
       for (int e = tid; e < TK * HD; e += TQ) {
@@ -70,7 +72,7 @@ __global__ __launch_bounds__(TQ) void fwd_f32_kernel(FwdArgs a) {
         const int64_t j = j0 + jj;
         float kvk = 0.f, kvv = 0.f;
         if (j < r.len_kv) {
-          const int64_t pos = r.kv_start + j * seg.stride;
+          const int64_t pos = piece_pos(r.kv_start, seg.stride, seg.run, j);
           kvk = kp[pos * G.ks[1] + c];
           kvv = vp[pos * G.vs[1] + c];
         }
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(TQ) void fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
         for (int c = 0; c < HD; ++c) s = fmaf(qv[c], ks[jj][c], s);
         s *= G.scale;
-        const bool vis = j < r.len_kv && j <= row + r.diag_offset;
+        const bool vis = j < r.len_kv && piece_pos(r.kv_start, seg.stride, seg.run, j) <= qpos;
         x[jj] = vis ? s : -INFINITY;
         mx = fmaxf(mx, x[jj]);
       }
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(TQ) void fwd_f32_kernel(FwdArgs a) {
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   const float lse = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
   if (OUT == 0) {
-    const int64_t pos = seg.q_start + row * seg.stride;
+    const int64_t pos = piece_pos(seg.q_start, seg.stride, seg.run, row);
     float *op = static_cast<float *>(a.o) + b * G.os[0] + pos * G.os[1] + h * G.os[2];
 #pragma unroll
     for (int c = 0; c < HD; ++c) op[c] = acc[c] * inv;

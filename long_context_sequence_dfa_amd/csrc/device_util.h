@@ -80,6 +80,15 @@ __device__ __forceinline__ void sload_words(uint64_t b, uint32_t (&w)[10]) {
   for (int i = 0; i < 8; ++i) w[i] = x[i];
   w[8] = y[0], w[9] = y[1];
 }
+__device__ __forceinline__ void sload_words(uint64_t b, uint32_t (&w)[12]) {
+  u32x8_t x;
+  u32x4 y;
+  asm("s_load_dwordx8 %0, %2, 0x0\n\ts_load_dwordx4 %1, %2, 0x20\n\ts_waitcnt lgkmcnt(0)"
+      : "=&s"(x), "=&s"(y)
+      : "s"(b));
+  for (int i = 0; i < 8; ++i) w[i] = x[i];
+  for (int i = 0; i < 4; ++i) w[8 + i] = y[i];
+}
 template <class T>
 __device__ __forceinline__ T ld_table(const T *p) {
   static_assert(sizeof(T) % 4 == 0, "table entries are whole dwords");

@@ -7,11 +7,39 @@
 
 namespace dfa {
 
-// One distinct query piece: local row i sits at global position
-// q_start + i*stride.  Its blocks (key pieces in ring-step order) are
-// kv[blk_begin, blk_begin + blk_count).
+// Global position of local row i of a piece: runs of `run` consecutive
+// tokens, consecutive runs `stride` apart (run = 1: start + i*stride).
+__host__ __device__ inline int64_t piece_pos(int64_t start, int64_t stride, int64_t run, int64_t i) {
+  return run == 1 ? start + i * stride : start + (i / run) * stride + i % run;
+}
+
+// Number of rows of a piece of `len` rows whose global position is <= x
+// (positions increase with the row index).
+__host__ __device__ inline int64_t piece_count_le(int64_t start, int64_t stride, int64_t run,
+                                                  int64_t len, int64_t x) {
+  if (x < start) return 0;
+  const int64_t d = x - start, u = d / stride, off = d - u * stride;
+  const int64_t n = u * run + (off + 1 < run ? off + 1 : run);
+  return n < len ? n : len;
+}
+
+// Distance between consecutive rows inside a 64-row tile of a piece (tiles
+// never straddle a run: run is 1 or a multiple of 64).
+__host__ __device__ inline int64_t piece_row_step(int64_t stride, int64_t run) {
+  return run == 1 ? stride : 1;
+}
+
+__host__ __device__ inline int64_t floor_div64(int64_t a, int64_t b) {
+  int64_t q = a / b;
+  if ((a % b != 0) && ((a < 0) != (b < 0))) --q;
+  return q;
+}
+
+// One distinct query piece (rows as in piece_pos).  Its blocks (key pieces
+// in ring-step order) are kv[blk_begin, blk_begin + blk_count); the key
+// pieces share the query piece's stride and run.
 struct QSeg {
-  int64_t q_start, len_q, stride;
+  int64_t q_start, len_q, stride, run;
   int64_t part_off;  // stepwise/block mode: float offset of this piece's partial buffer
   int32_t blk_begin, blk_count;
 };
@@ -25,7 +53,7 @@ struct KvRef {
 // One distinct key piece (backward, key-major walk) and the query pieces
 // that read it: q[blk_begin, blk_begin + blk_count).
 struct KvSeg {
-  int64_t kv_start, len_kv, stride;
+  int64_t kv_start, len_kv, stride, run;
   int32_t blk_begin, blk_count;
 };
 
@@ -58,6 +86,7 @@ struct FwdArgs {
   const Tile *tiles;
   int32_t n_tiles;
   int32_t out_mode;  // 0: final O/LSE at global rows; 1: fp32 partials per piece
+  int32_t runs;      // some piece is made of runs (run > 1)
   QSeg seg0;         // used when segs == nullptr (one block, no table)
   KvRef kv0;
 };
@@ -78,11 +107,12 @@ struct BwdArgs {
   const QRef *kvq;     // query pieces per key piece (dk/dv walk)
   const Tile *kvtiles;
   int32_t n_kvtiles;
+  int32_t runs;  // some piece is made of runs (run > 1)
 };
 
 // Row map of one partial buffer onto accumulator rows (stepwise merge).
 struct MergeItem {
-  int64_t q_start, len_q, stride, part_off;
+  int64_t q_start, len_q, stride, run, part_off;
 };
 
 // Tile shapes (rows per work item).

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(NT) void merge_items_kernel(float *o_acc, float *ls
   const int64_t prow = tid / C4;
   const int c = static_cast<int>(tid % C4);
   const int64_t bh = prow / it.len_q, i = prow % it.len_q;
-  const int64_t arow = bh * n + it.q_start + i * it.stride;
+  const int64_t arow = bh * n + piece_pos(it.q_start, it.stride, it.run, i);
   const float lp = lse_part[it.part_off + prow];
   const float la = lse_acc[arow];
   float wa, wp, lse;

@@ -9,6 +9,9 @@
 //             assignment).
 //   STRIPED   rank r owns positions r, r+P, r+2P, ... (Striped Attention
 //             Guide, "Mathematical Formulation of Token Striping").
+//   STRIPED with stripe blocks of B tokens: rank r owns the runs
+//             [(u*P + r)*B, (u*P + r + 1)*B), u = 0, 1, ... (the guide's
+//             block-striped variant).
 // At ring step s rank r holds the key/value shard of rank (r - s) mod P
 // (Striped Attention Guide, "Workload Balance Theorem").
 //
@@ -20,7 +23,10 @@
 // rank j (position n*P+j) iff n <= m when j <= r, iff n <= m-1 when j > r:
 // C*(C+1)/2 or C*(C-1)/2 pairs with diagonal offset 0 or -1 (the shifted
 // diagonal of the striped mask, Striped Attention Guide, "Algorithmic
-// Mechanics" 1, step 2).
+// Mechanics" 1, step 2).  With stripe blocks (R = C/B runs per rank), query
+// (run u, offset e) of rank r sees every key of the runs v < u of rank j, and
+// of run u all B keys when j < r, the first e+1 when j = r, none when j > r:
+// B*B*R*(R-1)/2 + R*(B*B, B*(B+1)/2 or 0) pairs.
 #include <cstring>
 #include <vector>
 
@@ -33,7 +39,7 @@ struct Emitter {
   int64_t capacity;
   int64_t n = 0;
   void emit(int64_t rank, int64_t step, int64_t kv_rank, int64_t q_start, int64_t kv_start,
-            int64_t len, int64_t stride, int64_t diag, int64_t pairs) {
+            int64_t len, int64_t stride, int64_t diag, int64_t pairs, int64_t run = 1) {
     if (out && n < capacity) {
       dfa_block &b = out[n];
       b.rank = rank;
@@ -46,6 +52,7 @@ struct Emitter {
       b.stride = stride;
       b.diag_offset = diag;
       b.pairs = pairs;
+      b.run = run;
     }
     ++n;
   }
@@ -111,6 +118,28 @@ extern "C" dfa_status dfa_schedule_build(int32_t kind, int64_t seqlen, int32_t n
     default:
       return DFA_E_UNSUPPORTED;
   }
+  *n_out = em.n;
+  if (out && em.n > capacity) return DFA_E_CAPACITY;
+  return DFA_OK;
+}
+
+extern "C" dfa_status dfa_schedule_build_striped_blocks(int64_t seqlen, int32_t n_ranks,
+                                                        int64_t stripe, dfa_block *out,
+                                                        int64_t capacity, int64_t *n_out) {
+  if (!n_out) return DFA_E_NULL;
+  if (seqlen < 1 || n_ranks < 1 || stripe < 1 || capacity < 0) return DFA_E_SHAPE;
+  const int64_t P = n_ranks, N = seqlen, B = stripe;
+  if (N % (P * B)) return DFA_E_SHAPE;
+  const int64_t C = N / P, R = C / B;
+  Emitter em{out, capacity};
+  for (int64_t r = 0; r < P; ++r)
+    for (int64_t s = 0; s < P; ++s) {
+      const int64_t j = ((r - s) % P + P) % P;
+      const int64_t same_run = j < r ? B * B : (j == r ? B * (B + 1) / 2 : 0);
+      const int64_t pairs = B * B * (R * (R - 1) / 2) + R * same_run;
+      if (pairs == 0) continue;
+      em.emit(r, s, j, r * B, j * B, C, P * B, floor_div(r - j, P), pairs, B);
+    }
   *n_out = em.n;
   if (out && em.n > capacity) return DFA_E_CAPACITY;
   return DFA_OK;

@@ -23,7 +23,7 @@ def rank_step_times(q, k, v, blocks, n_ranks: int, repeats: int = 3, scale=None,
     timed alone (median of ``repeats`` launches after one warm-up launch),
     summed over the blocks of its slot.  Slots without blocks cost 0."""
     import torch
-    arr = np.ascontiguousarray(blocks, dtype=np.int64).reshape(-1, 10)
+    arr = binding._blocks_arg(blocks)
     if stream is None:
         stream = torch.cuda.current_stream()
     B, _, Hq, D = q.shape
@@ -61,7 +61,7 @@ def measured_balance(times) -> dict:
 def pair_times(blocks, n_ranks: int):
     """The pair counts of the block list in the same [rank, step] layout (the
     cost model in which dfa_schedule_balance measures the bubble)."""
-    arr = np.ascontiguousarray(blocks, dtype=np.int64).reshape(-1, 10)
+    arr = binding._blocks_arg(blocks)
     t = np.zeros((n_ranks, n_ranks), dtype=np.float64)
     for blk in arr:
         t[int(blk[0]), int(blk[1])] += float(blk[9])

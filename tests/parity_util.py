@@ -14,6 +14,8 @@ gradients):
 """
 import numpy as np
 
+from oracle import schedule_ref as sr
+
 import oracle
 
 BF16_O_MAX, BF16_O_MEAN, BF16_LSE_MAX = 2e-2, 2e-3, 1e-3
@@ -63,13 +65,18 @@ def check_grad(g, r, rabs, dtype, what="", check_mean=True):
     return float(ratio.max())
 
 
+def _run(b):
+    return int(b[10]) if len(b) > 10 else 1
+
+
 def rows_of(blocks):
+    """Global query positions of a block list (runs as in dfa_block)."""
     if len(blocks) == 0:
         return np.zeros(0, dtype=np.int64)
-    return np.unique(np.concatenate([b[3] + b[7] * np.arange(b[5]) for b in blocks]))
+    return np.unique(np.concatenate([sr.positions((b[3], b[5], b[7], _run(b))) for b in blocks]))
 
 
 def kv_rows_of(blocks):
     if len(blocks) == 0:
         return np.zeros(0, dtype=np.int64)
-    return np.unique(np.concatenate([b[4] + b[7] * np.arange(b[6]) for b in blocks]))
+    return np.unique(np.concatenate([sr.positions((b[4], b[6], b[7], _run(b))) for b in blocks]))

@@ -56,7 +56,7 @@ int main(void) {{
                     D.q_strides.offset, D.o_strides.offset, D.softmax_scale.offset,
                     ctypes.sizeof(bd.DfaBalance), bd.DfaBalance.bubble.offset,
                     ctypes.sizeof(bd.DfaKernelMarks), bd.DfaKernelMarks.dv_begin.offset]
-    assert vals[0] == 80
+    assert vals[0] == 88
 
 
 def test_status_strings(bd):
@@ -143,6 +143,19 @@ def test_calls_reject_bad_arguments_before_launch(bd):
     wide.q_strides[:] = [1 << 26, (1 << 24) - 8, 128]
     assert L.dfa_attn_bwd(ctypes.byref(wide), arr, len(blocks), fake, fake, fake, fake, fake, fake,
                           fake, fake, fake, nul, 0, nul) == bd.DFA_E_WORKSPACE
+    # runs: a multiple of 64 (row tiles), whole runs, runs that do not overlap
+    sb = bd.dfa_schedule_build_striped_blocks(256, 2, 64)
+    sarr = np.ascontiguousarray(sb)
+    assert L.dfa_workspace_size(ctypes.byref(d), sarr.ctypes.data_as(ctypes.c_void_p), len(sb), 0,
+                                ctypes.byref(ctypes.c_size_t())) == 0
+    for field, val, want in (("run", 32, bd.DFA_E_UNSUPPORTED), ("len_q", 96, bd.DFA_E_SHAPE),
+                             ("stride", 32, bd.DFA_E_SHAPE), ("run", 0, bd.DFA_E_SHAPE)):
+        bad = sarr.copy()
+        bad[0, bd.BLOCK_FIELDS.index(field)] = val
+        if field == "stride":
+            bad[0, 8] = (bad[0, 3] - bad[0, 4]) // val  # keep diag_offset consistent
+        assert L.dfa_attn_fwd(ctypes.byref(d), bad.ctypes.data_as(ctypes.c_void_p), len(bad), 0, fake,
+                              fake, fake, fake, fake, nul, 0, nul) == want, field
     blk = bd.DfaBlock(*[int(x) for x in blocks[0]])
     assert L.dfa_attn_block_fwd(ctypes.byref(desc(bd, head_dim=32)), ctypes.byref(blk), fake, fake,
                                 fake, fake, fake, nul) == bd.DFA_E_UNSUPPORTED

@@ -92,11 +92,50 @@ def test_forward_backward_parity(dfa, case, dtype):
     if dtype == "f32" and (N > 1024 or Hq > 2):
         pytest.skip("fp32 path covered on the smaller cases")
     say(f"case: {sr.KIND_NAMES[kind]} N={N} P={P} B={B} Hq={Hq} Hkv={Hkv} D={D} rank={sub} {dtype}")
-    (q, k, v, do), (tq, tk, tv, tdo) = make(2000 + N + P, B, N, Hq, Hkv, D, dtype)
-    scale = 1 / np.sqrt(D)
     blocks = dfa.dfa_schedule_build(kind, N, P)
     if sub is not None:
         blocks = blocks[blocks[:, 0] == sub]
+    check_schedule(dfa, blocks, 2000 + N + P, N, B, Hq, Hkv, D, dtype)
+
+
+# stripe blocks of 64 or 128 tokens (the striped-attention page's recommended
+# block stripe sizes): N, P, stripe, batch, Hq, Hkv, d, subset rank
+STRIPE_CASES = [
+    (2048, 4, 64, 1, 2, 1, 128, None),
+    (1280, 4, 64, 2, 2, 2, 64, None),      # 5 runs per rank: a ragged 256-row workgroup
+    (4096, 8, 128, 1, 4, 2, 128, 5),       # one rank's share
+    (1536, 2, 128, 1, 2, 2, 128, 0),
+    (512, 8, 64, 1, 1, 1, 128, None),      # one run per rank
+]
+
+
+@pytest.mark.parametrize("case", STRIPE_CASES, ids=lambda c: "-".join(str(x) for x in c))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_stripe_block_parity(dfa, case, dtype):
+    N, P, stripe, B, Hq, Hkv, D, sub = case
+    if dtype == "f32" and (N > 1280 or Hq > 2):
+        # fp32 sums over > 1K keys drift past 1e-4 rms(g) in summation order
+        pytest.skip("fp32 path covered on the smaller cases")
+    say(f"case: stripe blocks N={N} P={P} stripe={stripe} B={B} Hq={Hq} Hkv={Hkv} D={D} "
+        f"rank={sub} {dtype}")
+    blocks = dfa.dfa_schedule_build_striped_blocks(N, P, stripe)
+    if sub is not None:
+        blocks = blocks[blocks[:, 0] == sub]
+    (q, k, v, _), (tq, tk, tv, _) = make(4000 + N + P, B, N, Hq, Hkv, D, dtype)
+    scale = 1 / np.sqrt(D)
+    for b in blocks[:6]:  # single-block partials (a diagonal run block among them)
+        op, lp = dfa.dfa_attn_block_fwd(tq, tk, tv, b)
+        torch.cuda.synchronize()
+        xo, xl = oracle.block_partial(q, k, v, scale, *b[3:8], run=b[10])
+        check_out(to_np(op), xo, to_np(lp), xl, dtype, f"block {b[:3]}")
+    check_schedule(dfa, blocks, 4000 + N + P, N, B, Hq, Hkv, D, dtype)
+
+
+def check_schedule(dfa, blocks, seed, N, B, Hq, Hkv, D, dtype):
+    """Fused and stepwise forward and the backward of a block list against the
+    oracle on the rows it touches; every other row must come out zero."""
+    (q, k, v, do), (tq, tk, tv, tdo) = make(seed, B, N, Hq, Hkv, D, dtype)
+    scale = 1 / np.sqrt(D)
     rows, krows = rows_of(blocks), kv_rows_of(blocks)
     ro, rl = oracle.attn_rows(q, k, v, scale, rows=rows)
     outs = {}

@@ -153,3 +153,59 @@ def test_schedule_errors(dfa):
     bad[0, 0] = 5
     with pytest.raises(bd.DfaError):
         dfa.dfa_schedule_balance(bad, 4)
+
+
+# ---- stripe blocks -----------------------------------------------------------
+def test_stripe_blocks_ownership_example():
+    # Striped Attention Guide, block-striped set: floor(i / B) mod P == p
+    toks = pieces_tokens_stripe(32, 4, 4)
+    assert [t.tolist() for t in toks] == [[0, 1, 2, 3, 16, 17, 18, 19], [4, 5, 6, 7, 20, 21, 22, 23],
+                                          [8, 9, 10, 11, 24, 25, 26, 27],
+                                          [12, 13, 14, 15, 28, 29, 30, 31]]
+
+
+def pieces_tokens_stripe(n, p, b):
+    return [np.concatenate([sr.positions(pc) for pc in rank])
+            for rank in sr.rank_pieces(sr.STRIPED_BLOCK, n, p, b)]
+
+
+@pytest.mark.parametrize("p,b", [(1, 64), (2, 3), (4, 64), (8, 128), (3, 5)])
+def test_stripe_block_coverage_and_balance(p, b):
+    n = 4 * p * b
+    blocks = sr.enumerate_schedule(sr.STRIPED_BLOCK, n, p, b)
+    assert blocks[:, 9].sum() == n * (n + 1) // 2
+    toks = np.sort(np.concatenate(pieces_tokens_stripe(n, p, b)))
+    assert np.array_equal(toks, np.arange(n))
+    # per rank: every earlier run of every rank (B*B pairs per run pair), plus
+    # in the same run index the whole runs of the r lower ranks and its own
+    # diagonal run -- so ranks differ by R*B*B per rank index
+    R = n // (p * b)
+    load = sr.balance(blocks, p)["rank_pairs"]
+    want = [p * b * b * R * (R - 1) // 2 + R * (r * b * b + b * (b + 1) // 2) for r in range(p)]
+    assert load.tolist() == want
+
+
+@pytest.mark.parametrize("n,p,b", [(1024, 4, 64), (2048, 8, 128), (96, 4, 3), (32768, 8, 64),
+                                   (8, 8, 1), (60, 3, 5)])
+def test_library_stripe_blocks_bit_exact(dfa, n, p, b):
+    ref = sr.enumerate_schedule(sr.STRIPED_BLOCK, n, p, b)
+    got = dfa.dfa_schedule_build_striped_blocks(n, p, b)
+    assert sr.to_bytes(got) == sr.to_bytes(ref), (n, p, b)
+    bal = dfa.dfa_schedule_balance(got, p)
+    assert bal["bubble"] == pytest.approx(sr.balance(ref, p)["bubble"], abs=1e-15)
+
+
+def test_stripe_one_is_token_striping(dfa):
+    for n, p in ((64, 4), (131072, 16)):
+        assert sr.to_bytes(dfa.dfa_schedule_build_striped_blocks(n, p, 1)) == \
+            sr.to_bytes(dfa.dfa_schedule_build(sr.STRIPED, n, p))
+
+
+def test_stripe_block_errors(dfa):
+    from long_context_sequence_dfa_amd import binding as bd
+    import ctypes
+    L = bd.lib()
+    n = ctypes.c_int64(-1)
+    assert L.dfa_schedule_build_striped_blocks(1000, 4, 64, None, 0, ctypes.byref(n)) == bd.DFA_E_SHAPE
+    assert L.dfa_schedule_build_striped_blocks(1024, 4, 0, None, 0, ctypes.byref(n)) == bd.DFA_E_SHAPE
+    assert L.dfa_schedule_build_striped_blocks(1024, 4, 64, None, 0, None) == bd.DFA_E_NULL
