@@ -43,7 +43,19 @@ WORKLOADS = {
                                             seed=1004, scaled=False, rank=0),
     "gqa-32-8-n256k-balanced-p32": dict(B=1, N=262144, Hq=32, Hkv=8, D=128, kind=1, P=32,
                                         seed=1005, scaled=False, rank=None),
+    # stripe blocks of 64 / 128 tokens (the striped-attention page's block sizes)
+    "llama7b-n32k-striped64-p8": dict(B=1, N=32768, Hq=32, Hkv=32, D=128, kind=2, P=8, seed=1003,
+                                      scaled=True, rank=None, stripe=64),
+    "llama7b-n32k-striped128-p8": dict(B=1, N=32768, Hq=32, Hkv=32, D=128, kind=2, P=8, seed=1003,
+                                       scaled=True, rank=None, stripe=128),
 }
+
+
+def schedule(dfa, wl):
+    """The workload's full block list (every rank)."""
+    if wl.get("stripe", 1) > 1:
+        return dfa.dfa_schedule_build_striped_blocks(wl["N"], wl["P"], wl["stripe"])
+    return dfa.dfa_schedule_build(wl["kind"], wl["N"], wl["P"])
 
 
 class HipEvents:
@@ -182,14 +194,14 @@ def main() -> int:
     q, k, v, do = inputs.workload_tensors(wl["seed"], B, N, Hq, Hkv, D, "bf16", qs, with_do=True)
     tq, tk, tv, tdo = (inputs.to_torch(x, "bf16", dev) for x in (q, k, v, do))
     del q, k, v, do
-    blocks = dfa.dfa_schedule_build(wl["kind"], N, wl["P"])
+    blocks = schedule(dfa, wl)
     if wl["rank"] is not None:
         blocks = blocks[blocks[:, 0] == wl["rank"]]
     pairs = int(blocks[:, 9].sum()) * B * Hq
     fwd_flops = 4.0 * D * pairs
     bwd_flops = 10.0 * D * pairs
     mode = dfa.DFA_FWD_FUSED if args.mode == "fused" else dfa.DFA_FWD_STEPWISE
-    bal = dfa.dfa_schedule_balance(dfa.dfa_schedule_build(wl["kind"], N, wl["P"]), wl["P"])
+    bal = dfa.dfa_schedule_balance(schedule(dfa, wl), wl["P"])
 
     o = torch.empty_like(tq)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
@@ -252,7 +264,7 @@ def main() -> int:
     # measured per-(rank, step) slot times of the forward: the idle bubble a
     # synchronous ring of P devices would see with these block costs
     from long_context_sequence_dfa_amd import timeline
-    full = dfa.dfa_schedule_build(wl["kind"], N, wl["P"])  # every rank, also for a rank's share
+    full = schedule(dfa, wl)  # every rank, also for a rank's share
     slot_ms = timeline.rank_step_times(tq, tk, tv, full, wl["P"], repeats=3, stream=stream)
     bubble_measured = timeline.measured_balance(slot_ms)["bubble"]
 
@@ -304,6 +316,7 @@ def main() -> int:
         "config": {"workload": args.workload, "global_batch": B, "seq_len": N, "heads_q": Hq,
                    "heads_kv": Hkv, "head_dim": D,
                    "schedule": {0: "ring", 1: "balanced", 2: "striped"}[wl["kind"]],
+                   "stripe": wl.get("stripe", 1),
                    "virtual_ranks": wl["P"], "rank_share": wl["rank"], "mode": args.mode,
                    "parallelism": "none: virtual ranks on one GPU"},
         "roofline": roofline,

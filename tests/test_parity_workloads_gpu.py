@@ -21,7 +21,10 @@ WORKLOADS = {
     "llama7b-n32k-balanced-p8": (32768, 32, 32, sr.BALANCED, 8, 1003, True, None, [0, 17]),
     "llama7b-n131k-striped-p16-rank0": (131072, 32, 32, sr.STRIPED, 16, 1004, False, 0, [5]),
     "gqa-32-8-n256k-balanced-p32": (262144, 32, 8, sr.BALANCED, 32, 1005, False, None, [1]),
+    # stripe blocks of 64 tokens at the Llama-7B shape (kind STRIPED_BLOCK)
+    "llama7b-n32k-striped64-p8": (32768, 32, 32, sr.STRIPED_BLOCK, 8, 1003, True, None, [9]),
 }
+STRIPE = {"llama7b-n32k-striped64-p8": 64}
 
 
 @pytest.fixture(scope="module")
@@ -44,7 +47,10 @@ def test_workload_sampled_parity(dfa, name):
     q, k, v, do = inputs.workload_tensors(seed, 1, N, Hq, Hkv, D, "bf16", qs, with_do=True)
     dev = torch.device("cuda:0")
     tq, tk, tv, tdo = (inputs.to_torch(x, "bf16", dev) for x in (q, k, v, do))
-    blocks = dfa.dfa_schedule_build(kind, N, P)
+    if kind == sr.STRIPED_BLOCK:
+        blocks = dfa.dfa_schedule_build_striped_blocks(N, P, STRIPE[name])
+    else:
+        blocks = dfa.dfa_schedule_build(kind, N, P)
     if rank is not None:
         blocks = blocks[blocks[:, 0] == rank]
     print(f"case: {name} forward + backward on the GPU ({len(blocks)} blocks)", flush=True)
@@ -56,7 +62,7 @@ def test_workload_sampled_parity(dfa, name):
 
     rows_all = rows_of(blocks)
     rng = np.random.default_rng(seed)
-    chunk = N // (2 * P) if kind == sr.BALANCED else N // P
+    chunk = {sr.BALANCED: N // (2 * P), sr.STRIPED_BLOCK: STRIPE.get(name, 1)}.get(kind, N // P)
     edges = [x for c in range(1, N // chunk) for x in (c * chunk - 1, c * chunk)]
     cand = np.concatenate([rng.choice(rows_all, 40, replace=False), rows_all[:4], rows_all[-4:],
                            np.array(edges[:8] + edges[-8:], dtype=np.int64)])
