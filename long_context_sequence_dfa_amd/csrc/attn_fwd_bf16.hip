@@ -1,6 +1,6 @@
 // attn_fwd_bf16.hip -- bf16 forward of blockwise causal attention on gfx950.
 //
-// One workgroup (4 waves) owns 128 query rows of one query piece, one batch
+// One workgroup (8 waves) owns 256 query rows of one query piece, one batch
 // entry and one query head.  It walks the piece's blocks in ring-step order
 // (the key/value shard a virtual rank holds at each step, read in place) and,
 // inside each block, the 64-key tiles that hold at least one visible key.
@@ -15,17 +15,16 @@
 //  * each wave computes S^T = K Q^T for 32 queries x 64 keys with
 //    v_mfma_f32_32x32x16_bf16, so every lane owns one query column: the row
 //    max and sum need only the lane's own 32 values plus one exchange with
-//    lane l^32;
+//    lane l^32 (v_permlane32_swap);
 //  * key rows enter the MFMA in a bit-swapped order (kperm) so that the S^T
 //    accumulator of a lane holds 8 consecutive keys per 16-key step -- exactly
 //    the B operand of O^T = V^T P^T, so P goes from accumulator to MFMA
 //    operand without touching LDS;
 //  * V^T operands come straight from the row-major V tile in LDS through
-//    ds_read_b64_tr_b16; the K and V tiles get different row pitches so that
-//    both the b128 reads of K and the transposing reads of V are free of
-//    bank conflicts;
-//  * K/V tiles are double-buffered in LDS; the next tile's global loads are
-//    issued before the current tile's MFMAs;
+//    ds_read_b64_tr_b16; the swizzled tile layout keeps both the b128 reads
+//    of K and the transposing reads of V free of bank conflicts;
+//  * K/V tiles stream through NS LDS stages by direct HBM->LDS loads issued
+//    NS - 1 tiles ahead (stream_lds.h); one barrier per tile;
 //  * the vector ALU is the scarce unit next to the MFMAs, so the softmax is
 //    kept lean: one FMA folds scale, log2(e) and the max into the exponent,
 //    and the running output is rescaled only when a row's max grows by more
@@ -219,6 +218,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
         s0 = mfma32(__builtin_bit_cast(bf16x8, ld16(kt + a_off + ks * 32)), qf[ks], s0);
         s1 = mfma32(__builtin_bit_cast(bf16x8, ld16(kt + a_off + 32 * RB + ks * 32)), qf[ks], s1);
       }
+      sched_lds_ahead<2 * KS, 4>();
       __builtin_amdgcn_s_setprio(0);
       // element i of s0 / s1 is key j0 + 32*(i/16) + 16*((i%16)/8) + 8g + i%8
       if ((dw < BK - 1) || (j0 + BK > cw.len_kv)) {
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int i = 1; i < 16; ++i)
         mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[i], s1[i]));
-      mx = __builtin_elementwise_maximum(mx, wave_swap32(mx)) * c;
+      mx = pair_max(mx) * c;
       // raise the reference max only when it grows by more than TAU: P <= 2^TAU
       if (__any(mx > m_run + TAU)) {
         const float m_new = __builtin_elementwise_maximum(m_run, mx);
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----
-  const float l_tot = l_run + wave_swap32(l_run);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY;
   const int64_t row = i0w + c32;

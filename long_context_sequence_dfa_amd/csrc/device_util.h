@@ -112,7 +112,30 @@ __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-__device__ __forceinline__ float wave_swap32(float x) { return __shfl_xor(x, 32); }
+// max / sum over the lane pair (l, l ^ 32), returned in both lanes: one
+// v_permlane32_swap (lanes 32..63 of the first operand trade places with
+// lanes 0..31 of the second) instead of a round trip through LDS
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Scheduling hint for a run of N LDS operand reads each feeding one of N
+// MFMAs: keep D reads in flight ahead of the products that consume them.
+template <int N, int D>
+__device__ __forceinline__ void sched_lds_ahead() {
+  __builtin_amdgcn_sched_group_barrier(0x100, D, 0);  // DS reads
+#pragma unroll
+  for (int i = 0; i < N - D; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, D, 0);
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) {
   return __uint_as_float(static_cast<uint32_t>(u) << 16);
