@@ -47,12 +47,12 @@ def _load():
                 build(force=True)
             lib = ctypes.CDLL(_LIB_PATH)
             i64, f64, p = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
-            lib.orc_attn_rows.argtypes = [i64] * 5 + [f64] + [p] * 3 + [i64, p, i64, p, p, p]
-            lib.orc_block_partial.argtypes = [i64] * 5 + [f64] + [p] * 3 + [i64] * 6 + [p, p]
+            lib.orc_attn_rows.argtypes = [i64] * 5 + [f64] + [p] * 3 + [i64, p, i64, p, p, p, p]
+            lib.orc_block_partial.argtypes = [i64] * 5 + [f64] + [p] * 3 + [i64] * 6 + [p, p, p]
             lib.orc_merge.argtypes = [i64, i64, i64, p, p, p, p]
-            lib.orc_grad_rows.argtypes = [i64] * 5 + [f64] + [p] * 4 + [i64, p, i64, p] + [p] * 5
+            lib.orc_grad_rows.argtypes = [i64] * 5 + [f64] + [p] * 4 + [i64, p, i64, p] + [p] * 6
             lib.orc_grad_cols.argtypes = ([i64] * 5 + [f64] + [p] * 4 + [i64, p, p, p]
-                                          + [i64, p, i64, p, p, p, p, p, p])
+                                          + [i64, p, i64, p, p, p, p, p, p, p])
             for f in ("orc_attn_rows", "orc_block_partial", "orc_merge", "orc_grad_rows",
                       "orc_grad_cols", "orc_num_threads"):
                 getattr(lib, f).restype = ctypes.c_int
@@ -85,36 +85,61 @@ def _dims(q, k):
     return B, N, Hq, Hkv, d
 
 
+def doc_ids(bounds, n):
+    """Document id of each of the n positions for packed documents given by
+    their cumulative boundaries (0 = bounds[0] < bounds[1] < ... = n):
+    positions [bounds[t], bounds[t+1]) form document t."""
+    b = [int(x) for x in np.asarray(bounds).reshape(-1)]
+    if len(b) < 2 or b[0] != 0 or b[-1] != n or any(b[t + 1] <= b[t] for t in range(len(b) - 1)):
+        raise ValueError("document bounds must rise strictly from 0 to N")
+    ids = np.empty(n, dtype=np.int64)
+    for t in range(len(b) - 1):
+        ids[b[t]:b[t + 1]] = t
+    return ids
+
+
+def _doc_arg(docs, n):
+    """(keep-alive array, pointer) for an optional document-bounds argument."""
+    if docs is None:
+        return None, ctypes.c_void_p(0)
+    ids = doc_ids(docs, n)
+    return ids, _ptr(ids)
+
+
 def num_threads() -> int:
     return int(_load().orc_num_threads())
 
 
-def attn_rows(q, k, v, scale, rows=None, heads=None):
+def attn_rows(q, k, v, scale, rows=None, heads=None, docs=None):
     """O1: causal attention for query rows ``rows`` (global positions) and
-    query heads ``heads``.  Returns o [B, n_heads, n_rows, d], lse [B, n_heads, n_rows]."""
+    query heads ``heads``; ``docs``: optional cumulative document boundaries
+    (attention stays inside each document).  Returns o [B, n_heads, n_rows, d],
+    lse [B, n_heads, n_rows]."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, N, Hq, Hkv, d = _dims(q, k)
+    keep, dp = _doc_arg(docs, N)
     rows = _i64(np.arange(N) if rows is None else rows)
     heads = _i64(np.arange(Hq) if heads is None else heads)
     o = np.zeros((B, heads.size, rows.size, d))
     lse = np.zeros((B, heads.size, rows.size))
     _check(_load().orc_attn_rows(B, N, Hq, Hkv, d, float(scale), _ptr(q), _ptr(k), _ptr(v),
-                                 rows.size, _ptr(rows), heads.size, _ptr(heads), _ptr(o), _ptr(lse)),
-           "attn_rows")
+                                 rows.size, _ptr(rows), heads.size, _ptr(heads), _ptr(o), _ptr(lse),
+                                 dp), "attn_rows")
     return o, lse
 
 
-def block_partial(q, k, v, scale, q_start, kv_start, len_q, len_kv, stride, run=1):
+def block_partial(q, k, v, scale, q_start, kv_start, len_q, len_kv, stride, run=1, docs=None):
     """O2: one block's normalised partial.  Local row i of either piece sits at
-    start + (i // run) * stride + i % run.  Returns o [B, Hq, len_q, d],
-    lse [B, Hq, len_q]."""
+    start + (i // run) * stride + i % run.  ``docs`` as in attn_rows.
+    Returns o [B, Hq, len_q, d], lse [B, Hq, len_q]."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, N, Hq, Hkv, d = _dims(q, k)
+    keep, dp = _doc_arg(docs, N)
     o = np.zeros((B, Hq, len_q, d))
     lse = np.zeros((B, Hq, len_q))
     _check(_load().orc_block_partial(B, N, Hq, Hkv, d, float(scale), _ptr(q), _ptr(k), _ptr(v),
                                      int(q_start), int(kv_start), int(len_q), int(len_kv),
-                                     int(stride), int(run), _ptr(o), _ptr(lse)), "block_partial")
+                                     int(stride), int(run), _ptr(o), _ptr(lse), dp), "block_partial")
     return o, lse
 
 
@@ -135,12 +160,13 @@ def merge(o_parts, lse_parts):
     return o, lse
 
 
-def grad_rows(q, k, v, dout, scale, rows=None, heads=None, with_abs=False):
+def grad_rows(q, k, v, dout, scale, rows=None, heads=None, with_abs=False, docs=None):
     """O5 row half.  Returns lse, D [B, n_heads, n_rows] and dq [B, n_heads, n_rows, d];
     with ``with_abs`` also A [B, n_heads, n_rows] and dq_abs like dq (the
-    rounding-error magnitudes tests use for tolerances)."""
+    rounding-error magnitudes tests use for tolerances).  ``docs`` as in attn_rows."""
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, N, Hq, Hkv, d = _dims(q, k)
+    keep, dp = _doc_arg(docs, N)
     rows = _i64(np.arange(N) if rows is None else rows)
     heads = _i64(np.arange(Hq) if heads is None else heads)
     lse = np.zeros((B, heads.size, rows.size))
@@ -153,18 +179,20 @@ def grad_rows(q, k, v, dout, scale, rows=None, heads=None, with_abs=False):
                                  _ptr(dout), rows.size, _ptr(rows), heads.size, _ptr(heads),
                                  _ptr(lse), _ptr(dd), _ptr(dq),
                                  _ptr(aa) if with_abs else nul,
-                                 _ptr(dq_abs) if with_abs else nul), "grad_rows")
+                                 _ptr(dq_abs) if with_abs else nul, dp), "grad_rows")
     if with_abs:
         return lse, dd, dq, aa, dq_abs
     return lse, dd, dq
 
 
-def grad_cols(q, k, v, dout, scale, rows, lse, dd, keys=None, kv_heads=None, aa=None):
+def grad_cols(q, k, v, dout, scale, rows, lse, dd, keys=None, kv_heads=None, aa=None, docs=None):
     """O5 column half.  ``lse`` and ``dd`` (and ``aa`` if given) are
     [B, Hq, n_rows] for the row set ``rows`` (every query head).  Returns
-    dk, dv [B, n_kv_heads, n_keys, d], plus dk_abs, dv_abs when ``aa`` is given."""
+    dk, dv [B, n_kv_heads, n_keys, d], plus dk_abs, dv_abs when ``aa`` is given.
+    ``docs`` as in attn_rows (and as given to grad_rows for lse, dd)."""
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, N, Hq, Hkv, d = _dims(q, k)
+    keep, dp = _doc_arg(docs, N)
     rows = _i64(rows)
     lse, dd = _f64(lse), _f64(dd)
     if lse.shape != (B, Hq, rows.size) or dd.shape != lse.shape:
@@ -185,24 +213,24 @@ def grad_cols(q, k, v, dout, scale, rows, lse, dd, keys=None, kv_heads=None, aa=
                                  _ptr(dk), _ptr(dv),
                                  _ptr(aa) if aa is not None else nul,
                                  _ptr(dk_abs) if aa is not None else nul,
-                                 _ptr(dv_abs) if aa is not None else nul), "grad_cols")
+                                 _ptr(dv_abs) if aa is not None else nul, dp), "grad_cols")
     if aa is not None:
         return dk, dv, dk_abs, dv_abs
     return dk, dv
 
 
-def attn_grads(q, k, v, dout, scale, rows=None, with_abs=False):
+def attn_grads(q, k, v, dout, scale, rows=None, with_abs=False, docs=None):
     """Full O5 for the query row set ``rows`` (default: every row): the loss is
     sum over those rows of dO.O.  Returns dq [B, Hq, n_rows, d] and
     dk, dv [B, Hkv, N, d]; with ``with_abs`` a second tuple of the matching
-    rounding-error magnitudes (dq_abs, dk_abs, dv_abs)."""
+    rounding-error magnitudes (dq_abs, dk_abs, dv_abs).  ``docs`` as in attn_rows."""
     q = _f64(q)
     B, N, Hq, d = q.shape
     rows = _i64(np.arange(N) if rows is None else rows)
     if not with_abs:
-        lse, dd, dq = grad_rows(q, k, v, dout, scale, rows=rows)
-        dk, dv = grad_cols(q, k, v, dout, scale, rows, lse, dd)
+        lse, dd, dq = grad_rows(q, k, v, dout, scale, rows=rows, docs=docs)
+        dk, dv = grad_cols(q, k, v, dout, scale, rows, lse, dd, docs=docs)
         return dq, dk, dv
-    lse, dd, dq, aa, dq_abs = grad_rows(q, k, v, dout, scale, rows=rows, with_abs=True)
-    dk, dv, dk_abs, dv_abs = grad_cols(q, k, v, dout, scale, rows, lse, dd, aa=aa)
+    lse, dd, dq, aa, dq_abs = grad_rows(q, k, v, dout, scale, rows=rows, with_abs=True, docs=docs)
+    dk, dv, dk_abs, dv_abs = grad_cols(q, k, v, dout, scale, rows, lse, dd, aa=aa, docs=docs)
     return (dq, dk, dv), (dq_abs, dk_abs, dv_abs)

@@ -33,6 +33,13 @@
  *    backward formulas; the functions below are the plain vector-Jacobian
  *    product of softmax attention written out element by element.
  *
+ *  - packed documents: when several documents are concatenated into one
+ *    sequence, a query attends only to keys of its own document (Striped
+ *    Attention Guide, "Production Deployment and Best Practices", item 3,
+ *    "Document Packing and Boundary Alignment").  Every function below takes
+ *    an optional doc[N] (document id of each position; NULL = one document)
+ *    and applies that rule on top of the causal one.
+ *
  * Natural logarithms throughout: LSE_i = m_i + ln(l_i).  A row with no visible
  * key has O = 0 and LSE = -inf.
  */
@@ -54,6 +61,12 @@ static double dot(const double *a, const double *b, int64_t d) {
   double s = 0.0;
   for (int64_t c = 0; c < d; ++c) s += a[c] * b[c];
   return s;
+}
+
+/* the key at position j is visible to the query at position i: not after it,
+ * and (with packed documents) in the same document */
+static int visible(int64_t i, int64_t j, const int64_t *doc) {
+  return j <= i && (doc == NULL || doc[j] == doc[i]);
 }
 
 static int dims_ok(int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int64_t d) {
@@ -91,12 +104,13 @@ static double attend_one(const double *qi, const double *kbase, const double *vb
  *   rows[r]  : global position of output row r (query at that position)
  *   heads[h] : query head of output head slot h
  *   o   : [B][n_heads][n_rows][d]     lse : [B][n_heads][n_rows]
- * Visible keys of the query at position i: every j in [0, i].
+ * Visible keys of the query at position i: every j in [0, i] (of i's
+ * document when doc != NULL).
  */
 int orc_attn_rows(int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int64_t d, double scale,
                   const double *q, const double *k, const double *v,
                   int64_t n_rows, const int64_t *rows, int64_t n_heads, const int64_t *heads,
-                  double *o, double *lse) {
+                  double *o, double *lse, const int64_t *doc) {
   if (!dims_ok(B, N, Hq, Hkv, d)) return ORC_EARG;
   for (int64_t r = 0; r < n_rows; ++r)
     if (rows[r] < 0 || rows[r] >= N) return ORC_EARG;
@@ -113,19 +127,20 @@ int orc_attn_rows(int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int64_t d, doub
 #pragma omp atomic write
       err = ORC_ENOMEM;
     } else {
-      for (int64_t j = 0; j < N; ++j) keys[j] = j;
 #pragma omp for schedule(dynamic, 1)
       for (int64_t w = 0; w < total; ++w) {
         int64_t b = w / (n_heads * n_rows);
         int64_t hs = (w / n_rows) % n_heads;
         int64_t r = w % n_rows;
-        int64_t h = heads[hs], hk = h / group, i = rows[r];
+        int64_t h = heads[hs], hk = h / group, i = rows[r], nk = 0;
+        for (int64_t j = 0; j <= i; ++j)
+          if (visible(i, j, doc)) keys[nk++] = j;
         const double *qi = vec(q, N, Hq, d, b, i, h);
         const double *kb = vec(k, N, Hkv, d, b, 0, hk);
         const double *vb = vec(v, N, Hkv, d, b, 0, hk);
         double *oi = o + ((b * n_heads + hs) * n_rows + r) * d;
         lse[(b * n_heads + hs) * n_rows + r] =
-            attend_one(qi, kb, vb, Hkv * d, keys, i + 1, d, scale, s_buf, oi);
+            attend_one(qi, kb, vb, Hkv * d, keys, nk, d, scale, s_buf, oi);
       }
     }
     free(s_buf);
@@ -147,15 +162,17 @@ static int64_t piece_position(int64_t start, int64_t stride, int64_t run, int64_
  * Query row i of the block sits at global position
  * piece_position(q_start, stride, run, i), key row j at
  * piece_position(kv_start, stride, run, j).  Key j is visible to query i iff
- * its global position is not after the query's (GlobalPos rule).  Each row is
- * normalised over the block's visible keys only.
+ * its global position is not after the query's (GlobalPos rule) and, with
+ * doc != NULL, both lie in the same document.  Each row is normalised over
+ * the block's visible keys only.
  *   o_part : [B][Hq][len_q][d]     lse_part : [B][Hq][len_q]
  */
 
 int orc_block_partial(int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int64_t d, double scale,
                       const double *q, const double *k, const double *v,
                       int64_t q_start, int64_t kv_start, int64_t len_q, int64_t len_kv,
-                      int64_t stride, int64_t run, double *o_part, double *lse_part) {
+                      int64_t stride, int64_t run, double *o_part, double *lse_part,
+                      const int64_t *doc) {
   if (!dims_ok(B, N, Hq, Hkv, d) || stride < 1 || run < 1 || len_q < 0 || len_kv < 0)
     return ORC_EARG;
   if (run > 1 && stride < run) return ORC_EARG;
@@ -179,7 +196,7 @@ int orc_block_partial(int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int64_t d, 
         int64_t qpos = piece_position(q_start, stride, run, i), nk = 0;
         for (int64_t j = 0; j < len_kv; ++j) {
           int64_t kpos = piece_position(kv_start, stride, run, j);
-          if (kpos <= qpos) keys[nk++] = kpos;
+          if (visible(qpos, kpos, doc)) keys[nk++] = kpos;
         }
         const double *qi = vec(q, N, Hq, d, b, qpos, h);
         const double *kb = vec(k, N, Hkv, d, b, 0, h / group);
@@ -234,7 +251,7 @@ int orc_merge(int64_t n_parts, int64_t n_rows, int64_t d,
 
 /*
  * O5, row half -- per query row of the loss  L = sum_{i in R} dO_i . O_i :
- *   P_ij  = e^{S_ij - LSE_i}           on visible pairs (j <= i), 0 elsewhere
+ *   P_ij  = e^{S_ij - LSE_i}           on visible pairs (j <= i, same document), 0 elsewhere
  *   dP_ij = dO_i . v_j
  *   D_i   = sum_j P_ij dP_ij
  *   dS_ij = P_ij (dP_ij - D_i)
@@ -249,7 +266,8 @@ int orc_merge(int64_t n_parts, int64_t n_rows, int64_t d,
 int orc_grad_rows(int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int64_t d, double scale,
                   const double *q, const double *k, const double *v, const double *dout,
                   int64_t n_rows, const int64_t *rows, int64_t n_heads, const int64_t *heads,
-                  double *lse, double *dd, double *dq, double *aa, double *dq_abs) {
+                  double *lse, double *dd, double *dq, double *aa, double *dq_abs,
+                  const int64_t *doc) {
   if (!dims_ok(B, N, Hq, Hkv, d)) return ORC_EARG;
   for (int64_t r = 0; r < n_rows; ++r)
     if (rows[r] < 0 || rows[r] >= N) return ORC_EARG;
@@ -277,7 +295,8 @@ int orc_grad_rows(int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int64_t d, doub
         /* scores and the row statistics */
         double m = -INFINITY;
         for (int64_t j = 0; j <= i; ++j) {
-          s_buf[j] = scale * dot(qi, vec(k, N, Hkv, d, b, j, hk), d);
+          /* a key of another document gets score -inf: P_ij = 0, dS_ij = 0 */
+          s_buf[j] = visible(i, j, doc) ? scale * dot(qi, vec(k, N, Hkv, d, b, j, hk), d) : -INFINITY;
           if (s_buf[j] > m) m = s_buf[j];
         }
         double l = 0.0;
@@ -327,8 +346,8 @@ int orc_grad_rows(int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int64_t d, doub
 
 /*
  * O5, column half -- per key row j and key/value head hk:
- *   dK_j = scale * sum_{h in group(hk)} sum_{i in R, i >= j} dS_ij q_i
- *   dV_j =         sum_{h in group(hk)} sum_{i in R, i >= j} P_ij dO_i
+ *   dK_j = scale * sum_{h in group(hk)} sum_{i in R, j visible to i} dS_ij q_i
+ *   dV_j =         sum_{h in group(hk)} sum_{i in R, j visible to i} P_ij dO_i
  * with P and dS rebuilt from the row statistics LSE_i and D_i that
  * orc_grad_rows produced for the same row set R.
  *   rows[r]          : global positions of R
@@ -344,7 +363,8 @@ int orc_grad_cols(int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int64_t d, doub
                   const double *q, const double *k, const double *v, const double *dout,
                   int64_t n_rows, const int64_t *rows, const double *lse, const double *dd,
                   int64_t n_keys, const int64_t *keys, int64_t n_kv_heads, const int64_t *kv_heads,
-                  double *dk, double *dv, const double *aa, double *dk_abs, double *dv_abs) {
+                  double *dk, double *dv, const double *aa, double *dk_abs, double *dv_abs,
+                  const int64_t *doc) {
   if (!dims_ok(B, N, Hq, Hkv, d)) return ORC_EARG;
   if ((dk_abs || dv_abs) && !(dk_abs && dv_abs && aa)) return ORC_EARG;
   for (int64_t r = 0; r < n_rows; ++r)
@@ -372,7 +392,7 @@ int orc_grad_cols(int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int64_t d, doub
       int64_t h = hk * group + g;
       for (int64_t r = 0; r < n_rows; ++r) {
         int64_t i = rows[r];
-        if (i < j) continue;
+        if (!visible(i, j, doc)) continue;
         const double *qi = vec(q, N, Hq, d, b, i, h);
         const double *doi = vec(dout, N, Hq, d, b, i, h);
         int64_t idx = (b * Hq + h) * n_rows + r;

@@ -225,3 +225,114 @@ def test_block_with_no_visible_key_row(orc):
     assert np.all(o[0, 0, 0] == 0) and np.isneginf(l[0, 0, 0])
     o1, l1 = orc.attn_rows(q[:, [4]], k[:, [3]], v[:, [3]], 0.5)  # row 1 sees only key 3
     np.testing.assert_allclose(o[0, 0, 1], o1[0, 0, 0], atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Packed documents (Striped Attention Guide, "Production Deployment and Best
+# Practices", item 3): a query attends only to keys of its own document.
+
+
+def random_bounds(rng, n, max_len):
+    """Cumulative document boundaries 0 = b0 < b1 < ... = n, lengths 1..max_len."""
+    b = [0]
+    while b[-1] < n:
+        b.append(min(n, b[-1] + int(rng.integers(1, max_len + 1))))
+    return np.array(b)
+
+
+DOC_CASES = [(np.array([0, 5, 6, 19, 31]), 31), (np.array([0, 1, 2, 3, 4, 5, 6]), 6),
+             (np.array([0, 40]), 40)]
+
+
+@pytest.mark.parametrize("bounds,N", DOC_CASES)
+def test_documents_equal_separate_sequences(orc, bounds, N):
+    """Document masking gives, document by document, plain causal attention of
+    that document alone (its own slice of q, k, v, positions restarting at 0)."""
+    B, Hq, Hkv, d = 2, 4, 2, 8
+    q, k, v = rand(B, N, Hq, d), rand(B, N, Hkv, d), rand(B, N, Hkv, d)
+    o, lse = orc.attn_rows(q, k, v, 0.4, docs=bounds)
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        od, ld = orc.attn_rows(q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], 0.4)
+        np.testing.assert_allclose(o[:, :, lo:hi], od, atol=1e-13, rtol=0)
+        np.testing.assert_allclose(lse[:, :, lo:hi], ld, atol=1e-13, rtol=0)
+
+
+def doc_mask(bounds, N):
+    """Boolean [N, N]: key j visible to query i (same document, j <= i)."""
+    did = np.searchsorted(bounds, np.arange(N), side="right") - 1
+    return (did[:, None] == did[None, :]) & np.tril(np.ones((N, N), dtype=bool))
+
+
+def test_documents_match_torch_sdpa_and_autograd(orc):
+    B, N, Hq, Hkv, d = 1, 37, 2, 1, 8
+    bounds = random_bounds(np.random.default_rng(5), N, 9)
+    q, k, v, do = rand(B, N, Hq, d), rand(B, N, Hkv, d), rand(B, N, Hkv, d), rand(B, N, Hq, d)
+    scale = 0.45
+    mask = torch.from_numpy(doc_mask(bounds, N))
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    o_ref = torch.nn.functional.scaled_dot_product_attention(
+        tq.permute(0, 2, 1, 3), tk.permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, 1),
+        tv.permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, 1), attn_mask=mask, scale=scale)
+    (o_ref * torch.from_numpy(do).permute(0, 2, 1, 3)).sum().backward()
+    o, _ = orc.attn_rows(q, k, v, scale, docs=bounds)
+    np.testing.assert_allclose(o, o_ref.detach().numpy(), atol=1e-12, rtol=0)
+    dq, dk, dv = orc.attn_grads(q, k, v, do, scale, docs=bounds)
+    np.testing.assert_allclose(dq, tq.grad.permute(0, 2, 1, 3).numpy(), atol=1e-11, rtol=0)
+    np.testing.assert_allclose(dk, tk.grad.permute(0, 2, 1, 3).numpy(), atol=1e-11, rtol=0)
+    np.testing.assert_allclose(dv, tv.grad.permute(0, 2, 1, 3).numpy(), atol=1e-11, rtol=0)
+
+
+def test_documents_gradients_equal_separate_sequences(orc):
+    B, N, Hq, Hkv, d = 1, 29, 2, 2, 4
+    bounds = np.array([0, 3, 4, 17, 29])
+    q, k, v, do = rand(B, N, Hq, d), rand(B, N, Hkv, d), rand(B, N, Hkv, d), rand(B, N, Hq, d)
+    dq, dk, dv = orc.attn_grads(q, k, v, do, 0.5, docs=bounds)
+    for lo, hi in zip(bounds[:-1], bounds[1:]):
+        s = slice(lo, hi)
+        gq, gk, gv = orc.attn_grads(q[:, s], k[:, s], v[:, s], do[:, s], 0.5)
+        np.testing.assert_allclose(dq[:, :, s], gq, atol=1e-12, rtol=0)
+        np.testing.assert_allclose(dk[:, :, s], gk, atol=1e-12, rtol=0)
+        np.testing.assert_allclose(dv[:, :, s], gv, atol=1e-12, rtol=0)
+
+
+def test_one_token_documents_closed_form(orc):
+    """Every token its own document: each query sees only its own key, so
+    O = v, LSE = scale q.k, dQ = dK = 0 (dP = D) and dV = dO summed over the
+    query heads of the group."""
+    B, N, Hq, Hkv, d = 1, 6, 4, 2, 4
+    q, k, v, do = rand(B, N, Hq, d), rand(B, N, Hkv, d), rand(B, N, Hkv, d), rand(B, N, Hq, d)
+    bounds = np.arange(N + 1)
+    o, lse = orc.attn_rows(q, k, v, 0.3, docs=bounds)
+    g = Hq // Hkv
+    for h in range(Hq):
+        np.testing.assert_allclose(o[0, h], v[0, :, h // g], atol=1e-15)
+        np.testing.assert_allclose(lse[0, h], 0.3 * np.sum(q[0, :, h] * k[0, :, h // g], -1), atol=1e-14)
+    dq, dk, dv = orc.attn_grads(q, k, v, do, 0.3, docs=bounds)
+    assert np.abs(dq).max() < 1e-14 and np.abs(dk).max() < 1e-14
+    for hk in range(Hkv):
+        np.testing.assert_allclose(dv[0, hk], do[0, :, hk * g:(hk + 1) * g].sum(1), atol=1e-14)
+
+
+@pytest.mark.parametrize("kind,N,P,stripe", [(sr.RING, 24, 4, 1), (sr.BALANCED, 24, 3, 1),
+                                             (sr.STRIPED, 24, 4, 1), (sr.STRIPED_BLOCK, 32, 2, 4)])
+def test_documents_merged_block_partials_equal_full(orc, kind, N, P, stripe):
+    B, Hq, Hkv, d = 1, 2, 1, 4
+    q, k, v = rand(B, N, Hq, d), rand(B, N, Hkv, d), rand(B, N, Hkv, d)
+    bounds = random_bounds(np.random.default_rng(N + P), N, 7)
+    full_o, full_l = orc.attn_rows(q, k, v, 0.6, docs=bounds)
+    merged_o = np.zeros_like(full_o)
+    merged_l = np.full_like(full_l, -np.inf)
+    for b in sr.enumerate_schedule(kind, N, P, stripe):
+        op, lp = orc.block_partial(q, k, v, 0.6, b[3], b[4], b[5], b[6], b[7], b[10], docs=bounds)
+        rows = sr.positions((b[3], b[5], b[7], b[10]))
+        mo, ml = orc.merge(np.stack([merged_o[:, :, rows], op]), np.stack([merged_l[:, :, rows], lp]))
+        merged_o[:, :, rows], merged_l[:, :, rows] = mo, ml
+    np.testing.assert_allclose(merged_o, full_o, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(merged_l, full_l, atol=1e-12, rtol=0)
+
+
+def test_document_bounds_are_validated(orc):
+    q = rand(1, 5, 1, 2)
+    for bad in ([0, 3], [1, 5], [0, 3, 3, 5], [0, 4, 2, 5]):
+        with pytest.raises(ValueError):
+            orc.attn_rows(q, q, q, 1.0, docs=bad)
