@@ -48,7 +48,22 @@ WORKLOADS = {
                                       scaled=True, rank=None, stripe=64),
     "llama7b-n32k-striped128-p8": dict(B=1, N=32768, Hq=32, Hkv=32, D=128, kind=2, P=8, seed=1003,
                                        scaled=True, rank=None, stripe=128),
+    # packed documents of 1K-8K tokens (the striped-attention page's document
+    # packing), attention kept inside each document
+    "llama7b-n32k-docs-balanced-p8": dict(B=1, N=32768, Hq=32, Hkv=32, D=128, kind=1, P=8,
+                                          seed=1003, scaled=True, rank=None, docs=(1024, 8192)),
+    "llama7b-n32k-docs-striped64-p8": dict(B=1, N=32768, Hq=32, Hkv=32, D=128, kind=2, P=8,
+                                           seed=1003, scaled=True, rank=None, stripe=64,
+                                           docs=(1024, 8192)),
 }
+
+
+def doc_bounds(wl):
+    """The workload's packed-document boundaries (host int64), or None."""
+    if "docs" not in wl:
+        return None
+    from long_context_sequence_dfa_amd import inputs
+    return inputs.doc_bounds(wl["seed"], wl["N"], *wl["docs"])
 
 
 def schedule(dfa, wl):
@@ -113,17 +128,6 @@ def stored_traffic(kernel: str, workload: str):
                 return None
             return float(parts[3])
     return None
-    for line in open(path):
-        parts = line.split()
-        if len(parts) == 4 and parts[0] == kernel and parts[1] == workload:
-            src = os.path.join(ROOT, "long_context_sequence_dfa_amd", "csrc", parts[2].split(":")[0])
-            want = parts[2].split(":")[1]
-            if not os.path.exists(src):
-                return None
-            if hashlib.sha256(open(src, "rb").read()).hexdigest()[:16] != want:
-                return None
-            return float(parts[3])
-    return None
 
 
 def cpu_baseline(wl: dict, budget_s: float = 20.0) -> dict:
@@ -140,23 +144,29 @@ def cpu_baseline(wl: dict, budget_s: float = 20.0) -> dict:
     qs = scale if wl["scaled"] else None
     best = None
     n = 1024
+    full_docs = doc_bounds(wl)
     while True:
         q = inputs.normal_tensor(wl["seed"], 0, (1, n, 1, D), "bf16", qs)
         k = inputs.normal_tensor(wl["seed"], 1, (1, n, 1, D), "bf16", qs)
         v = inputs.normal_tensor(wl["seed"], 2, (1, n, 1, D), "bf16", qs)
         do = inputs.normal_tensor(wl["seed"], 3, (1, n, 1, D), "bf16")
+        docs = None
+        if full_docs is not None:  # the documents cut at n
+            docs = np.append(full_docs[full_docs < n], n)
         t0 = time.perf_counter()
-        oracle.attn_rows(q, k, v, scale)
-        oracle.attn_grads(q, k, v, do, scale)
+        oracle.attn_rows(q, k, v, scale, docs=docs)
+        oracle.attn_grads(q, k, v, do, scale, docs=docs)
         dt = time.perf_counter() - t0
-        pairs = n * (n + 1) // 2
+        lens = [n] if docs is None else np.diff(docs)
+        pairs = sum(int(x) * (int(x) + 1) // 2 for x in lens)
         best = (n, dt, 14.0 * D * pairs / dt / 1e12)
         if dt * 4.2 > budget_s or n >= 32768:  # next doubling would exceed the budget
             break
         n *= 2
     n, dt, tflops = best
     return {"value": tflops, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"head 0, first {n} tokens (complete causal prefix), fwd + full grads, "
+            "sample": f"head 0, first {n} tokens (complete causal prefix"
+                      f"{', its documents' if full_docs is not None else ''}), fwd + full grads, "
                       f"fp64, {dt:.1f} s"}
 
 
@@ -194,19 +204,28 @@ def main() -> int:
     q, k, v, do = inputs.workload_tensors(wl["seed"], B, N, Hq, Hkv, D, "bf16", qs, with_do=True)
     tq, tk, tv, tdo = (inputs.to_torch(x, "bf16", dev) for x in (q, k, v, do))
     del q, k, v, do
+    from long_context_sequence_dfa_amd import timeline
     blocks = schedule(dfa, wl)
     if wl["rank"] is not None:
         blocks = blocks[blocks[:, 0] == wl["rank"]]
-    pairs = int(blocks[:, 9].sum()) * B * Hq
+    docs = doc_bounds(wl)
+    td = None if docs is None else torch.tensor(docs, dtype=torch.int32, device=dev)
+    if docs is None:
+        pairs = int(blocks[:, 9].sum()) * B * Hq
+        bal = dfa.dfa_schedule_balance(schedule(dfa, wl), wl["P"])
+    else:  # visible pairs and the ring balance under the document mask
+        pairs = int(timeline.doc_pair_counts(blocks, docs).sum()) * B * Hq
+        full = schedule(dfa, wl)
+        bal = timeline.measured_balance(timeline.pair_times(full, wl["P"],
+                                                            timeline.doc_pair_counts(full, docs)))
     fwd_flops = 4.0 * D * pairs
     bwd_flops = 10.0 * D * pairs
     mode = dfa.DFA_FWD_FUSED if args.mode == "fused" else dfa.DFA_FWD_STEPWISE
-    bal = dfa.dfa_schedule_balance(schedule(dfa, wl), wl["P"])
 
     o = torch.empty_like(tq)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(tq), torch.empty_like(tk), torch.empty_like(tv)
-    desc = dfa.make_desc(tq, tk, tv, o)
+    desc = dfa.make_desc(tq, tk, tv, o, docs=td)
     op_f = dfa.DFA_OP_FWD_FUSED if mode == dfa.DFA_FWD_FUSED else dfa.DFA_OP_FWD_STEPWISE
     ws_f = torch.empty(max(dfa.dfa_workspace_size(desc, blocks, op_f), 256), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(max(dfa.dfa_workspace_size(desc, blocks, dfa.DFA_OP_BWD), 256), dtype=torch.uint8,
@@ -220,13 +239,13 @@ def main() -> int:
     def step(m=None):
         if m is not None:
             ev.h.hipEventRecord(m[0], sp)
-        dfa.dfa_attn_fwd(tq, tk, tv, blocks, mode, o=o, lse=lse, workspace=ws_f)
+        dfa.dfa_attn_fwd(tq, tk, tv, blocks, mode, o=o, lse=lse, workspace=ws_f, docs=td)
         marks = None
         if m is not None:
             ev.h.hipEventRecord(m[1], sp)
             marks = binding.DfaKernelMarks(m[2], m[3], m[4], m[5], m[6])
         dfa.dfa_attn_bwd(tq, tk, tv, o, tdo, lse, blocks, dq=dq, dk=dk, dv=dv, workspace=ws_b,
-                         marks=marks)
+                         marks=marks, docs=td)
 
     if args.calibrate_copy:
         # one plain device copy of known size: the scale for HBM byte counters
@@ -251,21 +270,20 @@ def main() -> int:
                          device=dev)
     o_alt = torch.empty_like(tq)
     lse_alt = torch.empty_like(lse)
-    dfa.dfa_attn_fwd(tq, tk, tv, blocks, alt_mode, o=o_alt, lse=lse_alt, workspace=ws_alt)
+    dfa.dfa_attn_fwd(tq, tk, tv, blocks, alt_mode, o=o_alt, lse=lse_alt, workspace=ws_alt, docs=td)
     e0, e1 = ev.create(), ev.create()
     n_alt = 3
     ev.h.hipEventRecord(e0, sp)
     for _ in range(n_alt):
-        dfa.dfa_attn_fwd(tq, tk, tv, blocks, alt_mode, o=o_alt, lse=lse_alt, workspace=ws_alt)
+        dfa.dfa_attn_fwd(tq, tk, tv, blocks, alt_mode, o=o_alt, lse=lse_alt, workspace=ws_alt, docs=td)
     ev.h.hipEventRecord(e1, sp)
     alt_ms = ev.elapsed(e0, e1) / n_alt
     del ws_alt, o_alt, lse_alt
 
     # measured per-(rank, step) slot times of the forward: the idle bubble a
     # synchronous ring of P devices would see with these block costs
-    from long_context_sequence_dfa_amd import timeline
     full = schedule(dfa, wl)  # every rank, also for a rank's share
-    slot_ms = timeline.rank_step_times(tq, tk, tv, full, wl["P"], repeats=3, stream=stream)
+    slot_ms = timeline.rank_step_times(tq, tk, tv, full, wl["P"], repeats=3, stream=stream, docs=td)
     bubble_measured = timeline.measured_balance(slot_ms)["bubble"]
 
     per = {name: float(np.mean([ev.elapsed(m[a], m[b]) for m in ev_all]))
@@ -317,6 +335,8 @@ def main() -> int:
                    "heads_kv": Hkv, "head_dim": D,
                    "schedule": {0: "ring", 1: "balanced", 2: "striped"}[wl["kind"]],
                    "stripe": wl.get("stripe", 1),
+                   "documents": None if docs is None else {"count": len(docs) - 1,
+                                                            "lengths": list(wl["docs"])},
                    "virtual_ranks": wl["P"], "rank_share": wl["rank"], "mode": args.mode,
                    "parallelism": "none: virtual ranks on one GPU"},
         "roofline": roofline,

@@ -125,6 +125,17 @@ typedef struct dfa_block {
  * page, "variants").  Gradients use their primal's strides: dq like q, dk like
  * k, dv like v, d_o like o.  LSE arrays are fp32 [batch][heads_q][seqlen],
  * contiguous, natural logarithm.
+ *
+ * Packed documents (Striped Attention Guide, "Production Deployment and Best
+ * Practices", item 3): when doc_bounds is not NULL the sequence is a
+ * concatenation of n_docs documents and a query attends only to keys of its
+ * own document (on top of the causal rule).  doc_bounds is a DEVICE array of
+ * n_docs + 1 int32 positions, doc_bounds[0] = 0 < doc_bounds[1] < ... <
+ * doc_bounds[n_docs] = seqlen; document t holds positions [doc_bounds[t],
+ * doc_bounds[t+1]).  The same boundaries apply to every batch entry.  The
+ * host cannot read them: calls check only 1 <= n_docs <= seqlen < 2^31
+ * (else DFA_E_SHAPE); boundaries that break the rule above give unspecified
+ * results (no out-of-bounds access).  With doc_bounds NULL, n_docs is ignored.
  */
 typedef struct dfa_attn_desc {
   int32_t dtype;         /* DFA_BF16 or DFA_F32 */
@@ -138,6 +149,8 @@ typedef struct dfa_attn_desc {
   int64_t k_strides[3];
   int64_t v_strides[3];
   int64_t o_strides[3];
+  const int32_t *doc_bounds; /* device, n_docs + 1 entries, or NULL (one document) */
+  int64_t n_docs;
 } dfa_attn_desc;
 
 /*

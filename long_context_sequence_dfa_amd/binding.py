@@ -43,7 +43,8 @@ class DfaAttnDesc(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
                 ("seqlen", ctypes.c_int64),
                 ("q_strides", ctypes.c_int64 * 3), ("k_strides", ctypes.c_int64 * 3),
-                ("v_strides", ctypes.c_int64 * 3), ("o_strides", ctypes.c_int64 * 3)]
+                ("v_strides", ctypes.c_int64 * 3), ("o_strides", ctypes.c_int64 * 3),
+                ("doc_bounds", ctypes.c_void_p), ("n_docs", ctypes.c_int64)]
 
 
 class DfaBalance(ctypes.Structure):
@@ -168,10 +169,21 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def make_desc(q, k, v, o=None, scale=None) -> DfaAttnDesc:
-    """Descriptor for tensors laid out [batch, token, head, head_dim]."""
+def make_desc(q, k, v, o=None, scale=None, docs=None) -> DfaAttnDesc:
+    """Descriptor for tensors laid out [batch, token, head, head_dim].
+    ``docs``: optional int32 device tensor of cumulative document boundaries
+    (0 = docs[0] < ... < docs[-1] = N) for packed documents; the caller keeps
+    it alive until the work has run."""
     B, N, Hq, D = q.shape
     d = DfaAttnDesc()
+    if docs is not None:
+        import torch
+        if docs.dtype != torch.int32 or docs.dim() != 1 or not docs.is_contiguous() or docs.numel() < 2:
+            raise ValueError("docs must be a contiguous 1-D int32 tensor of >= 2 boundaries")
+        if docs.device != q.device:
+            raise ValueError("docs must be on the tensors' device")
+        d.doc_bounds = docs.data_ptr()
+        d.n_docs = docs.numel() - 1
     d.dtype = _dtype_code(q)
     d.batch, d.heads_q, d.heads_kv, d.head_dim = B, Hq, k.shape[2], D
     d.seqlen = N
@@ -213,11 +225,12 @@ def _workspace(desc, blocks, op, device, workspace):
 
 
 # ---------------------------------------------------------------- kernels
-def dfa_attn_block_fwd(q, k, v, block, o_part=None, lse_part=None, scale=None, stream=None):
+def dfa_attn_block_fwd(q, k, v, block, o_part=None, lse_part=None, scale=None, stream=None,
+                       docs=None):
     """One block's normalised partial: o_part fp32 [B, Hq, len_q, d], lse_part fp32 [B, Hq, len_q]."""
     import torch
     blk = DfaBlock(*[int(x) for x in _blocks_arg(block)[0]])
-    desc = make_desc(q, k, v, scale=scale)
+    desc = make_desc(q, k, v, scale=scale, docs=docs)
     B, _, Hq, D = q.shape
     if o_part is None:
         o_part = torch.empty((B, Hq, blk.len_q, D), dtype=torch.float32, device=q.device)
@@ -246,7 +259,7 @@ def dfa_lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
 
 
 def dfa_attn_fwd(q, k, v, blocks, mode=DFA_FWD_FUSED, o=None, lse=None, workspace=None,
-                 scale=None, stream=None):
+                 scale=None, stream=None, docs=None):
     """Forward over a block list.  Returns (o [B, N, Hq, d], lse fp32 [B, Hq, N])."""
     import torch
     B, N, Hq, D = q.shape
@@ -254,7 +267,7 @@ def dfa_attn_fwd(q, k, v, blocks, mode=DFA_FWD_FUSED, o=None, lse=None, workspac
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    desc = make_desc(q, k, v, o, scale)
+    desc = make_desc(q, k, v, o, scale, docs)
     arr = _blocks_arg(blocks)
     op = DFA_OP_FWD_FUSED if mode == DFA_FWD_FUSED else DFA_OP_FWD_STEPWISE
     ws, nbytes = _workspace(desc, arr, op, q.device, workspace)
@@ -265,7 +278,7 @@ def dfa_attn_fwd(q, k, v, blocks, mode=DFA_FWD_FUSED, o=None, lse=None, workspac
 
 
 def dfa_attn_bwd(q, k, v, o, d_o, lse, blocks, dq=None, dk=None, dv=None, workspace=None,
-                 scale=None, stream=None, marks=None):
+                 scale=None, stream=None, marks=None, docs=None):
     """Gradients (dq, dk, dv) of the forward over the same block list.
     ``marks``: optional DfaKernelMarks of hipEvent_t handles (dfa_attn_bwd_ex)."""
     import torch
@@ -276,7 +289,7 @@ def dfa_attn_bwd(q, k, v, o, d_o, lse, blocks, dq=None, dk=None, dv=None, worksp
     dv = torch.empty_like(v) if dv is None else dv
     if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
         raise ValueError("gradients must have their primal's strides")
-    desc = make_desc(q, k, v, o, scale)
+    desc = make_desc(q, k, v, o, scale, docs)
     arr = _blocks_arg(blocks)
     ws, nbytes = _workspace(desc, arr, DFA_OP_BWD, q.device, workspace)
     args = (ctypes.byref(desc), arr.ctypes.data_as(ctypes.c_void_p), arr.shape[0], _ptr(q),

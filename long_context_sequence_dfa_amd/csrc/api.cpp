@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -53,6 +54,8 @@ dfa_status check_desc(const dfa_attn_desc *d) {
   if (d->batch < 1 || d->heads_q < 1 || d->heads_kv < 1 || d->seqlen < 1) return DFA_E_SHAPE;
   if (d->heads_q % d->heads_kv) return DFA_E_SHAPE;
   if (!std::isfinite(d->softmax_scale)) return DFA_E_SHAPE;
+  if (d->doc_bounds && (d->n_docs < 1 || d->n_docs > d->seqlen || d->seqlen > INT32_MAX))
+    return DFA_E_SHAPE;
   const int64_t elems16 = d->dtype == DFA_BF16 ? 8 : 4;  // elements per 16 bytes
   const int64_t *all[4] = {d->q_strides, d->k_strides, d->v_strides, d->o_strides};
   for (auto s : all)
@@ -274,6 +277,8 @@ dfa::Geom make_geom(const dfa_attn_desc *d) {
   g.group = d->heads_q / d->heads_kv;
   g.scale = d->softmax_scale;
   g.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+  g.docs = d->doc_bounds;
+  g.n_docs = d->doc_bounds ? static_cast<int32_t>(d->n_docs) : 0;
   return g;
 }
 

@@ -16,11 +16,18 @@
 //    registers as MFMA operands), walks every block that reads its key piece
 //    and every query head of its group, and computes S = Q K^T, dP = dO V^T,
 //    dV^T += dO^T P and dK^T += Q^T dS.  Each lane owns one key column.
+// With packed documents (Striped Attention Guide, "Production Deployment and
+// Best Practices", item 3) a pair is kept only inside one document: the
+// query-major kernel masks keys before the row's document start, the
+// key-major ones queries at or after the key's document end, and both skip
+// the tiles no row of the workgroup can see.
 // Both stream 64-row K/V (or Q/dO) tiles through NS LDS stages with direct
 // loads issued NS - 1 tiles ahead (stream_lds.h); transposed operands come
 // from ds_read_b64_tr_b16 on the row-major tiles.
 #include "dfa_internal.h"
 #include "stream_lds.h"
+
+#include <stdint.h>
 
 namespace dfa {
 namespace {
@@ -36,7 +43,7 @@ static_assert(DQ_BQ == 32 * NW, "one 32-query column block per wave");
 
 // RUNS: pieces made of runs (stripe blocks), visibility from global
 // positions; otherwise rows start + i*stride and each block's diagonal.
-template <int HD, bool RUNS>
+template <int HD, bool RUNS, bool DOCS>
 __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
   using TL = Tile64<HD>;
   static_assert(TL::ROWS == DQ_BK, "key tiles are 64 rows");
@@ -64,13 +71,26 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
   const int64_t rs = RUNS ? piece_row_step(seg.stride, seg.run) : seg.stride;  // row step in a tile
   const int64_t q_last = RUNS ? pos_of(seg.q_start, iend - 1) : 0;
   const int64_t gq_w = RUNS ? pos_of(seg.q_start, i0w) : 0;
+  // packed documents: this lane's row sees keys at positions >= qlo only;
+  // qlo_w is the wave's largest bound, wlo the workgroup's smallest
+  int32_t qlo = 0, qlo_w = 0;
+  int64_t wlo = 0;
+  if constexpr (DOCS) {
+    int64_t lo, hi_;
+    const int64_t r = i0w + c32;
+    doc_range(G.docs, G.n_docs, pos_of(seg.q_start, r < seg.len_q ? r : seg.len_q - 1), lo, hi_);
+    qlo = static_cast<int32_t>(lo);
+    qlo_w = __builtin_amdgcn_readlane(qlo, 31);
+    doc_range(G.docs, G.n_docs, pos_of(seg.q_start, i0), lo, hi_);
+    wlo = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(lo));
+  }
 
   const char *kb = static_cast<const char *>(a.k) + 2 * (b * G.ks[0] + hk * G.ks[2]);
   const char *vb = static_cast<const char *>(a.v) + 2 * (b * G.vs[0] + hk * G.vs[2]);
 
-  // walk over (block, key tile)
+  // walk over (block, key tile); t0 skips tiles before wlo
   struct Walk {
-    int64_t kv_start, len_kv, diag, ntiles;
+    int64_t kv_start, len_kv, diag, ntiles, t0;
   };
   auto walk = [&](int k) {  // key tiles holding a key at or before the last row
     const KvRef r = ld_table(a.qkv + seg.blk_begin + k);
@@ -81,33 +101,34 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
       hi = iend + r.diag_offset;
       if (hi > r.len_kv) hi = r.len_kv;
     }
-    return Walk{r.kv_start, r.len_kv, r.diag_offset, hi > 0 ? (hi + DQ_BK - 1) / DQ_BK : 0};
+    const int64_t t0 = wlo > 0 ? piece_count_le(r.kv_start, seg.stride, seg.run, r.len_kv, wlo - 1) / DQ_BK : 0;
+    return Walk{r.kv_start, r.len_kv, r.diag_offset, hi > 0 ? (hi + DQ_BK - 1) / DQ_BK : 0, t0};
   };
   const int nblk = seg.blk_count;
   auto first = [&](int &k_, Walk &w_) {
     while (k_ < nblk) {
       w_ = walk(k_);
-      if (w_.ntiles > 0) return;
+      if (w_.ntiles > w_.t0) return;
       ++k_;
     }
   };
   auto next = [&](int &k_, int64_t &t_, Walk &w_) {
     if (++t_ < w_.ntiles) return;
-    t_ = 0;
     ++k_;
     first(k_, w_);
+    t_ = w_.t0;
   };
   int k = 0;
-  int64_t t = 0;
-  Walk cw{0, 0, 0, 0};
+  Walk cw{0, 0, 0, 0, 0};
   first(k, cw);
+  int64_t t = cw.t0;
 
   // K and V stream
   const TileStream<HD, NW> ld(wave, lane, 2 * G.ks[1] * rs, 2 * G.vs[1] * rs);
   const int per_tile = 2 * ld.count();
   const unsigned lds0 = lds_addr(smem);
   int kl = k;
-  int64_t tl_ = 0;
+  int64_t tl_ = t;
   Walk lw = cw;
   int issued = 0;
   auto issue = [&](int stage) {
@@ -167,14 +188,25 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
     if (dw + 31 >= 0) {
       const char *kt = smem + (it % NS) * STAGE;
       const char *vt = kt + TB;
-      const bool need_mask = (dw < DQ_BK - 1) || (j0 + DQ_BK > cw.len_kv);
+      const int64_t gk = DOCS ? pos_of(cw.kv_start, j0) : 0;  // position of key 0 of the tile
+      const bool need_mask = (dw < DQ_BK - 1) || (j0 + DQ_BK > cw.len_kv) || (DOCS && gk < qlo_w);
       int x = 0;
+      unsigned span = 0;
       if (need_mask) {
         // element i of half kh is local key jj = 32kh + 16(i/8) + 8g + i%8,
-        // visible iff jj <= lim; x = 8g - lim
+        // visible iff lo <= jj <= lim (causal rule and piece end give lim,
+        // the row's document start gives lo); x = 8g - lo
         const int64_t lim64 = c32 + dw, len64 = cw.len_kv - 1 - j0;
         const int64_t m64 = lim64 < len64 ? lim64 : len64;
-        x = 8 * g - static_cast<int>(m64 < -1 ? -1 : (m64 > DQ_BK ? DQ_BK : m64));
+        const int lim = static_cast<int>(m64 < -1 ? -1 : (m64 > DQ_BK ? DQ_BK : m64));
+        int lo = 0;
+        if (DOCS && qlo > gk) {
+          const unsigned ahead = static_cast<unsigned>(qlo - gk), step = static_cast<unsigned>(rs);
+          const unsigned l = (ahead + step - 1) / step;
+          lo = l > static_cast<unsigned>(DQ_BK) ? DQ_BK : static_cast<int>(l);
+        }
+        span = static_cast<unsigned>(lim + 1 > lo ? lim + 1 - lo : 0);
+        x = 8 * g - lo;
       }
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {  // two halves of 32 keys
@@ -192,7 +224,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
         if (need_mask) {
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (x + 32 * kh + 16 * (i / 8) + (i % 8) > 0) sv[i] = -INFINITY;
+            if (static_cast<unsigned>(x + 32 * kh + 16 * (i / 8) + (i % 8)) >= span) sv[i] = -INFINITY;
         }
         bf16x8 dsb[2];
 #pragma unroll
@@ -238,7 +270,7 @@ static_assert(KV_BK == 32 * NW, "one 32-key column block per wave");
 // SIMD and hide each other's LDS and exponent latency; S is recomputed in both.
 constexpr int KV_DV = 1, KV_DK = 2;
 
-template <int HD, int MODE, bool RUNS>
+template <int HD, int MODE, bool RUNS, bool DOCS>
 __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
   using TL = Tile64<HD>;
   static_assert(TL::ROWS == KV_BQ, "query tiles are 64 rows");
@@ -272,6 +304,20 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
   // global positions of the workgroup's and this wave's first key
   const int64_t gk0 = RUNS ? pos_of(seg.kv_start, j0) : 0;
   const int64_t gk_w = RUNS ? pos_of(seg.kv_start, j0w) : 0;
+  // packed documents: queries at positions >= khi cannot see this lane's
+  // key; khi_w is the wave's smallest bound (its first key), whi the
+  // workgroup's largest (its last key) -- positions rise with the row index
+  int32_t khi = INT32_MAX, khi_w = INT32_MAX;
+  int64_t whi = INT64_MAX;
+  if constexpr (DOCS) {
+    int64_t lo_, hi;
+    doc_range(G.docs, G.n_docs, pos, lo_, hi);
+    khi = static_cast<int32_t>(hi);
+    khi_w = __builtin_amdgcn_readfirstlane(khi);
+    const int64_t jl = (j0 + KV_BK < seg.len_kv ? j0 + KV_BK : seg.len_kv) - 1;
+    doc_range(G.docs, G.n_docs, pos_of(seg.kv_start, jl), lo_, hi);
+    whi = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(hi));
+  }
 
   // walk over (group head, block, query tile)
   struct Walk {
@@ -289,9 +335,12 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
       lo = j0 - r.diag_offset;
       if (lo < 0) lo = 0;
     }
-    if (lo < r.len_q) {
+    // the query rows before the first position after the last key's document
+    const int64_t hi = DOCS ? piece_count_le(r.q_start, seg.stride, seg.run, r.len_q, whi - 1)
+                                       : r.len_q;
+    if (lo < hi) {
       w.t0 = lo / KV_BQ;
-      w.t1 = (r.len_q + KV_BQ - 1) / KV_BQ;
+      w.t1 = (hi + KV_BQ - 1) / KV_BQ;
     }
     return w;
   };
@@ -394,12 +443,22 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
       const float *lt = reinterpret_cast<const float *>(qt + 2 * TB);
       const float *ddt = lt + KV_BQ;
       // local query qq (0..63) of the tile is kept iff lo <= qq < hi
-      const bool need_mask = (dw < 31) || (qi0 + KV_BQ > cw.len_q);
+      // packed documents: global position of the tile's first and last query
+      const int64_t gq0 = DOCS ? pos_of(cw.q_start, qi0) : 0;
+      const int64_t gql = DOCS ? pos_of(cw.q_start, (qi0 + KV_BQ < cw.len_q ? qi0 + KV_BQ : cw.len_q) - 1)
+                                   : 0;
+      const bool need_mask = (dw < 31) || (qi0 + KV_BQ > cw.len_q) || (DOCS && gql >= khi_w);
       int lo = 0, hi = KV_BQ;
       if (need_mask) {
         const int64_t lo64 = c32 - dw, hi64 = cw.len_q - qi0;
         lo = static_cast<int>(lo64 < 0 ? 0 : (lo64 > KV_BQ ? KV_BQ : lo64));
         hi = static_cast<int>(hi64 > KV_BQ ? KV_BQ : hi64);
+        if (DOCS) {  // queries of the tile before the end of the key's document
+          const int dh = khi <= gq0 ? 0
+                                    : static_cast<int>((static_cast<unsigned>(khi - gq0) + static_cast<unsigned>(rs) - 1) /
+                                                       static_cast<unsigned>(rs));
+          hi = dh < hi ? dh : hi;
+        }
       }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {  // two halves of 32 query rows
@@ -416,10 +475,11 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
         // scores become -inf (probability 0)
         if (need_mask) {
           const int x = 8 * g - lo;  // qq - lo without the element's constant part
+          const unsigned span = static_cast<unsigned>(hi > lo ? hi - lo : 0);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const unsigned rel = static_cast<unsigned>(x + 32 * mt + 16 * (i / 8) + (i % 8));
-            if (rel >= static_cast<unsigned>(hi - lo)) s[i] = -INFINITY;
+            if (rel >= span) s[i] = -INFINITY;
           }
         }
         bf16x8 ob[2];
@@ -472,32 +532,48 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
 
 }  // namespace
 
+template <int HD, bool RUNS>
+void launch_dq_variant(const BwdArgs &a, dim3 gr, hipStream_t s) {
+  if (a.g.n_docs)
+    hipLaunchKernelGGL((dq_bf16_kernel<HD, RUNS, true>), gr, dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((dq_bf16_kernel<HD, RUNS, false>), gr, dim3(NT), 0, s, a);
+}
+
 hipError_t launch_bwd_dq_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const dim3 gr(static_cast<unsigned>(grid)), bl(NT);
+  const dim3 gr(static_cast<unsigned>(grid));
   if (hd == 128) {
     if (a.runs)
-      hipLaunchKernelGGL((dq_bf16_kernel<128, true>), gr, bl, 0, s, a);
+      launch_dq_variant<128, true>(a, gr, s);
     else
-      hipLaunchKernelGGL((dq_bf16_kernel<128, false>), gr, bl, 0, s, a);
+      launch_dq_variant<128, false>(a, gr, s);
   } else if (hd == 64) {
     if (a.runs)
-      hipLaunchKernelGGL((dq_bf16_kernel<64, true>), gr, bl, 0, s, a);
+      launch_dq_variant<64, true>(a, gr, s);
     else
-      hipLaunchKernelGGL((dq_bf16_kernel<64, false>), gr, bl, 0, s, a);
+      launch_dq_variant<64, false>(a, gr, s);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <int HD, int MODE, bool RUNS>
+void launch_dkdv_docs(const BwdArgs &a, dim3 gr, hipStream_t s) {
+  if (a.g.n_docs)
+    hipLaunchKernelGGL((dkdv_bf16_kernel<HD, MODE, RUNS, true>), gr, dim3(NT), 0, s, a);
+  else
+    hipLaunchKernelGGL((dkdv_bf16_kernel<HD, MODE, RUNS, false>), gr, dim3(NT), 0, s, a);
+}
+
 template <int HD, int MODE>
 void launch_dkdv_variant(const BwdArgs &a, dim3 gr, hipStream_t s) {
   if (a.runs)
-    hipLaunchKernelGGL((dkdv_bf16_kernel<HD, MODE, true>), gr, dim3(NT), 0, s, a);
+    launch_dkdv_docs<HD, MODE, true>(a, gr, s);
   else
-    hipLaunchKernelGGL((dkdv_bf16_kernel<HD, MODE, false>), gr, dim3(NT), 0, s, a);
+    launch_dkdv_docs<HD, MODE, false>(a, gr, s);
 }
 
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs &a, int hd, int64_t grid, int which, hipStream_t s) {

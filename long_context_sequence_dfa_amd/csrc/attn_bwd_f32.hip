@@ -6,11 +6,15 @@
 //   dS_ij = P_ij (dP_ij - D_i) with D_i = rowsum(dO_i * O_i),
 //   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,
 //   dV_j = sum_i P_ij dO_i.
+// Packed documents restrict every pair to one document (Striped Attention
+// Guide, "Production Deployment and Best Practices", item 3).
 // Two kernels, neither with atomics: a query-major one owns dQ rows and walks
 // each query piece's blocks; a key-major one owns dK/dV rows, walks the blocks
 // that read its key piece and sums over the query heads of its group.
 #include "device_util.h"
 #include "dfa_internal.h"
+
+#include <stdint.h>
 
 namespace dfa {
 namespace {
@@ -41,6 +45,14 @@ __global__ __launch_bounds__(TQ) void dq_f32_kernel(BwdArgs a) {
   float qv[HD], dov[HD], acc[HD];
   float lse = 0.f, dd = 0.f;
   int64_t pos = 0;
+  // packed documents: keys before qlo are invisible to this row, before wlo
+  // to every row of the workgroup
+  int64_t qlo = 0, wlo = 0, dhi;
+  if (G.n_docs) {
+    doc_range(G.docs, G.n_docs, piece_pos(seg.q_start, seg.stride, seg.run, valid ? row : rlast), qlo, dhi);
+    doc_range(G.docs, G.n_docs, piece_pos(seg.q_start, seg.stride, seg.run, tl.tile * static_cast<int64_t>(TQ)),
+              wlo, dhi);
+  }
   if (valid) {
     pos = piece_pos(seg.q_start, seg.stride, seg.run, row);
 #pragma unroll
@@ -61,7 +73,8 @@ __global__ __launch_bounds__(TQ) void dq_f32_kernel(BwdArgs a) {
     // keys at or before the tile's last query row
     const int64_t hi = piece_count_le(r.kv_start, seg.stride, seg.run, r.len_kv,
                                       piece_pos(seg.q_start, seg.stride, seg.run, rlast));
-    for (int64_t j0 = 0; j0 < hi; j0 += TS) {
+    const int64_t jlo = piece_count_le(r.kv_start, seg.stride, seg.run, r.len_kv, wlo - 1);
+    for (int64_t j0 = jlo / TS * TS; j0 < hi; j0 += TS) {
       __syncthreads();
       for (int e = tid; e < TS * HD; e += TQ) {
         const int jj = e / HD, c = e % HD;
@@ -79,7 +92,9 @@ __global__ __launch_bounds__(TQ) void dq_f32_kernel(BwdArgs a) {
       if (!valid) continue;
       for (int jj = 0; jj < TS; ++jj) {
         const int64_t j = j0 + jj;
-        if (j >= r.len_kv || piece_pos(r.kv_start, seg.stride, seg.run, j) > pos) continue;
+        if (j >= r.len_kv) continue;
+        const int64_t kpos = piece_pos(r.kv_start, seg.stride, seg.run, j);
+        if (kpos > pos || kpos < qlo) continue;
         float s = 0.f, dp = 0.f;
 #pragma unroll
         for (int c = 0; c < HD; ++c) {
@@ -119,6 +134,14 @@ __global__ __launch_bounds__(TK) void dkdv_f32_kernel(BwdArgs a) {
   const float *vp = static_cast<const float *>(a.v) + b * G.vs[0] + hk * G.vs[2];
   float kv_[HD], vv[HD], dk[HD], dv[HD];
   int64_t pos = 0;
+  // packed documents: queries at or after khi cannot see this key, at or
+  // after whi no key of the workgroup (the largest bound: positions rise)
+  int64_t khi = INT64_MAX, whi = INT64_MAX, dlo;
+  if (G.n_docs) {
+    const int64_t jl = (j0 + TK < seg.len_kv ? j0 + TK : seg.len_kv) - 1;
+    doc_range(G.docs, G.n_docs, piece_pos(seg.kv_start, seg.stride, seg.run, valid ? j : jl), dlo, khi);
+    doc_range(G.docs, G.n_docs, piece_pos(seg.kv_start, seg.stride, seg.run, jl), dlo, whi);
+  }
   if (valid) {
     pos = piece_pos(seg.kv_start, seg.stride, seg.run, j);
 #pragma unroll
@@ -143,7 +166,8 @@ __global__ __launch_bounds__(TK) void dkdv_f32_kernel(BwdArgs a) {
       // the first query row at or after the tile's first key
       const int64_t lo = piece_count_le(r.q_start, seg.stride, seg.run, r.len_q,
                                         piece_pos(seg.kv_start, seg.stride, seg.run, j0) - 1);
-      for (int64_t i0 = lo; i0 < r.len_q; i0 += TS) {
+      const int64_t iend = G.n_docs ? piece_count_le(r.q_start, seg.stride, seg.run, r.len_q, whi - 1) : r.len_q;
+      for (int64_t i0 = lo; i0 < iend; i0 += TS) {
         __syncthreads();
         for (int e = tid; e < TS * HD; e += TK) {
           const int ii = e / HD, c = e % HD;
@@ -167,7 +191,9 @@ __global__ __launch_bounds__(TK) void dkdv_f32_kernel(BwdArgs a) {
         if (!valid) continue;
         for (int ii = 0; ii < TS; ++ii) {
           const int64_t i = i0 + ii;
-          if (i >= r.len_q || pos > piece_pos(r.q_start, seg.stride, seg.run, i)) continue;
+          if (i >= r.len_q) continue;
+          const int64_t qpos = piece_pos(r.q_start, seg.stride, seg.run, i);
+          if (pos > qpos || qpos >= khi) continue;
           float s = 0.f, dp = 0.f;
 #pragma unroll
           for (int c = 0; c < HD; ++c) {

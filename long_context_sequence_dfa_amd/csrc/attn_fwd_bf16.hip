@@ -9,7 +9,10 @@
 // Guide, "Algorithmic Mechanics" 1, steps 1-6), then normalises once at the
 // end (step 7) and emits LSE = m + ln l.  Tiles past the causal limit are
 // never visited and only tiles that straddle the diagonal evaluate the mask
-// ("Algorithmic Mechanics" 2, intra- vs inter-block masking).
+// ("Algorithmic Mechanics" 2, intra- vs inter-block masking).  With packed
+// documents a key before the first position of the row's document is masked
+// too, and tiles before the first row's document are skipped (same page,
+// "Production Deployment and Best Practices", item 3).
 //
 // gfx950 mapping:
 //  * each wave computes S^T = K Q^T for 32 queries x 64 keys with
@@ -46,15 +49,18 @@ static_assert(BQ == 32 * NW, "one 32-query column block per wave");
 
 struct BlockWalk {
   int64_t kv_start, len_kv, diag, ntiles;
+  int64_t t0;  // first tile with a key visible to some row (packed documents)
 };
 
 // The key piece of block k; ntiles covers every key at or before the
-// workgroup's last query row (local row iend-1, global position q_last).
-// RUNS: pieces made of runs (stripe blocks), visibility from global
-// positions; otherwise rows start + i*stride and the block's diagonal.
+// workgroup's last query row (local row iend-1, global position q_last), t0
+// skips the tiles before wlo, the first position of the first row's document
+// (0 without packed documents).  RUNS: pieces made of runs (stripe blocks),
+// visibility from global positions; otherwise rows start + i*stride and the
+// block's diagonal.
 template <bool TABLE, bool RUNS>
 __device__ __forceinline__ BlockWalk block_walk(const FwdArgs &a, const QSeg &seg, int k,
-                                                int64_t iend, int64_t q_last) {
+                                                int64_t iend, int64_t q_last, int64_t wlo) {
   KvRef r;
   if constexpr (TABLE)
     r = ld_table(a.kv + seg.blk_begin + k);
@@ -72,12 +78,13 @@ __device__ __forceinline__ BlockWalk block_walk(const FwdArgs &a, const QSeg &se
     if (hi > r.len_kv) hi = r.len_kv;
   }
   w.ntiles = hi > 0 ? (hi + BK - 1) / BK : 0;
+  w.t0 = wlo > 0 ? piece_count_le(r.kv_start, seg.stride, seg.run, r.len_kv, wlo - 1) / BK : 0;
   return w;
 }
 
 // TABLE: the query piece and its blocks come from the work tables (fused and
 // stepwise walks); otherwise from seg0/kv0 (one block).
-template <int HD, int OUT, bool TABLE, bool RUNS>
+template <int HD, int OUT, bool TABLE, bool RUNS, bool DOCS>
 __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   using TL = Tile64<HD>;
   static_assert(TL::ROWS == BK, "key tiles are 64 rows");
@@ -121,6 +128,20 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   // only the mask's row comparisons use it)
   const int64_t gq_w = RUNS ? pos_of(seg.q_start, i0w) : 0;
   const float c = G.scale_log2;
+  // packed documents: this lane's row sees keys at positions >= qlo only;
+  // qlo_w is the largest bound of the wave (its last row), wlo the smallest
+  // of the workgroup (its first row) -- positions rise with the row index
+  int32_t qlo = 0, qlo_w = 0;
+  int64_t wlo = 0;
+  if constexpr (DOCS) {
+    int64_t lo, hi_;
+    const int64_t r = i0w + c32;
+    doc_range(G.docs, G.n_docs, pos_of(seg.q_start, r < seg.len_q ? r : seg.len_q - 1), lo, hi_);
+    qlo = static_cast<int32_t>(lo);
+    qlo_w = __builtin_amdgcn_readlane(qlo, 31);
+    doc_range(G.docs, G.n_docs, pos_of(seg.q_start, i0), lo, hi_);
+    wlo = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(lo));
+  }
 
   const char *qb = static_cast<const char *>(a.q) + 2 * (b * G.qs[0] + h * G.qs[2]);
   const char *kb = static_cast<const char *>(a.k) + 2 * (b * G.ks[0] + hk * G.ks[2]);
@@ -146,28 +167,28 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   const int nblk = TABLE ? seg.blk_count : 1;
   auto first = [&](int &k_, BlockWalk &w_) {
     while (k_ < nblk) {
-      w_ = block_walk<TABLE, RUNS>(a, seg, k_, iend, q_last);
-      if (w_.ntiles > 0) return;
+      w_ = block_walk<TABLE, RUNS>(a, seg, k_, iend, q_last, wlo);
+      if (w_.ntiles > w_.t0) return;
       ++k_;
     }
   };
   auto next = [&](int &k_, int64_t &t_, BlockWalk &w_) {
     if (++t_ < w_.ntiles) return;
-    t_ = 0;
     ++k_;
     first(k_, w_);
+    t_ = w_.t0;
   };
   int k = 0;
-  int64_t t = 0;
-  BlockWalk cw{0, 0, 0, 0};
+  BlockWalk cw{0, 0, 0, 0, 0};
   first(k, cw);
+  int64_t t = cw.t0;
 
   // ---- K/V stream: NS LDS stages, the load cursor runs NS - 1 tiles ahead ----
   const TileStream<HD, NW> ld(wave, lane, 2 * G.ks[1] * rs, 2 * G.vs[1] * rs);
   const int per_tile = 2 * ld.count();
   const unsigned lds0 = lds_addr(smem);
   int kl = k;
-  int64_t tl = 0;
+  int64_t tl = t;
   BlockWalk lw = cw;
   int issued = 0;
   auto issue = [&](int stage) {
@@ -221,17 +242,38 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
       sched_lds_ahead<2 * KS, 4>();
       __builtin_amdgcn_s_setprio(0);
       // element i of s0 / s1 is key j0 + 32*(i/16) + 16*((i%16)/8) + 8g + i%8
-      if ((dw < BK - 1) || (j0 + BK > cw.len_kv)) {
-        // key j0 + jj is visible iff jj <= lim; x = 8g - lim
+      // (global position of key jj of the tile: gk + jj * rs)
+      const int64_t gk = DOCS ? pos_of(cw.kv_start, j0) : 0;
+      if ((dw < BK - 1) || (j0 + BK > cw.len_kv) || (DOCS && gk < qlo_w)) {
+        // key j0 + jj is visible iff lo <= jj <= lim: lim from the causal
+        // rule and the piece's end, lo from the row's document start
         const int64_t lim64 = c32 + dw;
         const int64_t len64 = cw.len_kv - 1 - j0;
         const int64_t m64 = lim64 < len64 ? lim64 : len64;
-        const int x = 8 * g - static_cast<int>(m64 < -1 ? -1 : (m64 > BK ? BK : m64));
+        const int lim = static_cast<int>(m64 < -1 ? -1 : (m64 > BK ? BK : m64));
+        if constexpr (DOCS) {
+          int lo = 0;
+          if (qlo > gk) {
+            const unsigned ahead = static_cast<unsigned>(qlo - gk), step = static_cast<unsigned>(rs);
+            const unsigned l = (ahead + step - 1) / step;
+            lo = l > static_cast<unsigned>(BK) ? BK : static_cast<int>(l);
+          }
+          const unsigned span = static_cast<unsigned>(lim + 1 > lo ? lim + 1 - lo : 0);
+          const int x = 8 * g - lo;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kc = 16 * (i / 8) + (i % 8);
-          if (x + kc > 0) s0[i] = -INFINITY;
-          if (x + kc + 32 > 0) s1[i] = -INFINITY;
+          for (int i = 0; i < 16; ++i) {
+            const int kc = 16 * (i / 8) + (i % 8);
+            if (static_cast<unsigned>(x + kc) >= span) s0[i] = -INFINITY;
+            if (static_cast<unsigned>(x + kc + 32) >= span) s1[i] = -INFINITY;
+          }
+        } else {
+          const int x = 8 * g - lim;  // key jj = kc + 8g is masked iff jj > lim
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kc = 16 * (i / 8) + (i % 8);
+            if (x + kc > 0) s0[i] = -INFINITY;
+            if (x + kc + 32 > 0) s1[i] = -INFINITY;
+          }
         }
       }
       // row max with the NaN-propagating maximum: v_maximum3_f32 needs no
@@ -319,15 +361,23 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
 
 }  // namespace
 
-template <int HD, bool RUNS>
-void launch_fwd_variant(const FwdArgs &a, dim3 gr, hipStream_t s) {
+template <int HD, bool RUNS, bool DOCS>
+void launch_fwd_docs(const FwdArgs &a, dim3 gr, hipStream_t s) {
   const dim3 bl(NT);
   if (a.out_mode == 0)
-    hipLaunchKernelGGL((fwd_bf16_kernel<HD, 0, true, RUNS>), gr, bl, 0, s, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<HD, 0, true, RUNS, DOCS>), gr, bl, 0, s, a);
   else if (a.segs)
-    hipLaunchKernelGGL((fwd_bf16_kernel<HD, 1, true, RUNS>), gr, bl, 0, s, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<HD, 1, true, RUNS, DOCS>), gr, bl, 0, s, a);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<HD, 1, false, RUNS>), gr, bl, 0, s, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<HD, 1, false, RUNS, DOCS>), gr, bl, 0, s, a);
+}
+
+template <int HD, bool RUNS>
+void launch_fwd_variant(const FwdArgs &a, dim3 gr, hipStream_t s) {
+  if (a.g.n_docs)
+    launch_fwd_docs<HD, RUNS, true>(a, gr, s);
+  else
+    launch_fwd_docs<HD, RUNS, false>(a, gr, s);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int hd, int64_t grid, hipStream_t s) {

@@ -6,7 +6,9 @@
 // running max, sum and output in registers while the workgroup streams
 // 64-key K/V tiles of the piece's blocks, in ring-step order, through LDS.
 // The update is the online-softmax rescaling of the Striped Attention Guide,
-// "Algorithmic Mechanics" 1, steps 1-7.
+// "Algorithmic Mechanics" 1, steps 1-7.  With packed documents a key is also
+// invisible when it lies before the first position of the query's document
+// (same page, "Production Deployment and Best Practices", item 3).
 #include "device_util.h"
 #include "dfa_internal.h"
 
@@ -41,6 +43,13 @@ __global__ __launch_bounds__(TQ) void fwd_f32_kernel(FwdArgs a) {
   const bool valid = row < seg.len_q;
   const int64_t rlast = ((qt + 1) * TQ < seg.len_q ? (qt + 1) * TQ : seg.len_q) - 1;
   const int64_t qpos = piece_pos(seg.q_start, seg.stride, seg.run, valid ? row : rlast);
+  // packed documents: this row sees keys at positions >= qlo only; wlo is
+  // the bound of the workgroup's first row (the smallest: positions rise)
+  int64_t qlo = 0, wlo = 0, dhi;
+  if (G.n_docs) {
+    doc_range(G.docs, G.n_docs, qpos, qlo, dhi);
+    doc_range(G.docs, G.n_docs, piece_pos(seg.q_start, seg.stride, seg.run, qt * TQ), wlo, dhi);
+  }
 
   const float *qp = static_cast<const float *>(a.q) + b * G.qs[0] + h * G.qs[2];
   const float *kp = static_cast<const float *>(a.k) + b * G.ks[0] + hk * G.ks[2];
@@ -65,7 +74,9 @@ __global__ __launch_bounds__(TQ) void fwd_f32_kernel(FwdArgs a) {
     // keys at or before the tile's last query row
     const int64_t hi = piece_count_le(r.kv_start, seg.stride, seg.run, r.len_kv,
                                       piece_pos(seg.q_start, seg.stride, seg.run, rlast));
-    for (int64_t j0 = 0; j0 < hi; j0 += TK) {
+    // keys before wlo are invisible to every row of the workgroup
+    const int64_t jlo = piece_count_le(r.kv_start, seg.stride, seg.run, r.len_kv, wlo - 1);
+    for (int64_t j0 = jlo / TK * TK; j0 < hi; j0 += TK) {
       __syncthreads();
       for (int e = tid; e < TK * HD; e += TQ) {
         const int jj = e / HD, c = e % HD;
@@ -88,7 +99,8 @@ __global__ __launch_bounds__(TQ) void fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
         for (int c = 0; c < HD; ++c) s = fmaf(qv[c], ks[jj][c], s);
         s *= G.scale;
-        const bool vis = j < r.len_kv && piece_pos(r.kv_start, seg.stride, seg.run, j) <= qpos;
+        const int64_t kpos = piece_pos(r.kv_start, seg.stride, seg.run, j);
+        const bool vis = j < r.len_kv && kpos <= qpos && kpos >= qlo;
         x[jj] = vis ? s : -INFINITY;
         mx = fmaxf(mx, x[jj]);
       }

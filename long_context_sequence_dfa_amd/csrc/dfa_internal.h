@@ -73,7 +73,25 @@ struct Geom {
   int32_t batch, hq, hkv, group;  // group = hq / hkv
   float scale_log2;               // softmax scale * log2(e)
   float scale;                    // softmax scale
+  const int32_t *docs;            // packed documents: n_docs + 1 ascending bounds, or null
+  int32_t n_docs;                 // 0: one document (plain causal)
 };
+
+// Packed documents: [lo, hi) = the document holding global position p, by
+// binary search over the n + 1 cumulative bounds (document t holds
+// [b[t], b[t+1])).  Every load stays inside b[0..n] whatever b holds.
+__device__ inline void doc_range(const int32_t *b, int n, int64_t p, int64_t &lo, int64_t &hi) {
+  int l = 0, r = n;
+  while (r - l > 1) {
+    const int m = (l + r) >> 1;
+    if (b[m] <= p)
+      l = m;
+    else
+      r = m;
+  }
+  lo = b[l];
+  hi = b[l + 1];
+}
 
 // Forward over query pieces (fused walk, stepwise rounds, single block).
 struct FwdArgs {

@@ -115,3 +115,26 @@ def workload_tensors(seed: int, B: int, N: int, Hq: int, Hkv: int, D: int, dtype
         return q, k, v
     do = normal_tensor(seed, 3, (B, N, Hq, D), dtype)
     return q, k, v, do
+
+
+DOC_STREAM_ID = 4  # stream key id of document lengths
+
+
+def doc_bounds(seed: int, n: int, min_len: int, max_len: int) -> np.ndarray:
+    """Cumulative boundaries of packed documents over n positions: document
+    lengths drawn uniformly from [min_len, max_len] (splitmix64 output t of
+    stream mix(seed * 16 + 4), length = min_len + output mod (max_len -
+    min_len + 1)) until they cover n; the last document is cut at n.
+    Returns int64 [0, b1, ..., n]."""
+    if not (1 <= min_len <= max_len) or n < 1:
+        raise ValueError("need 1 <= min_len <= max_len and n >= 1")
+    key = stream_key(seed, DOC_STREAM_ID)
+    span = np.uint64(max_len - min_len + 1)
+    bounds, pos, t = [0], 0, 0
+    while pos < n:
+        with np.errstate(over="ignore"):
+            x = _mix(np.array([key + np.uint64(t + 1) * GAMMA], dtype=np.uint64))[0]
+        pos = min(n, pos + min_len + int(x % span))
+        bounds.append(pos)
+        t += 1
+    return np.array(bounds, dtype=np.int64)

@@ -18,10 +18,12 @@ import numpy as np
 from . import binding
 
 
-def rank_step_times(q, k, v, blocks, n_ranks: int, repeats: int = 3, scale=None, stream=None):
+def rank_step_times(q, k, v, blocks, n_ranks: int, repeats: int = 3, scale=None, stream=None,
+                    docs=None):
     """Milliseconds per (rank, step) slot, shape [n_ranks, n_ranks]: each block
     timed alone (median of ``repeats`` launches after one warm-up launch),
-    summed over the blocks of its slot.  Slots without blocks cost 0."""
+    summed over the blocks of its slot.  Slots without blocks cost 0.
+    ``docs``: optional int32 device tensor of packed-document boundaries."""
     import torch
     arr = binding._blocks_arg(blocks)
     if stream is None:
@@ -33,10 +35,10 @@ def rank_step_times(q, k, v, blocks, n_ranks: int, repeats: int = 3, scale=None,
         rank, step, len_q = int(blk[0]), int(blk[1]), int(blk[5])
         op = torch.empty((B, Hq, len_q, D), dtype=torch.float32, device=q.device)
         lp = torch.empty((B, Hq, len_q), dtype=torch.float32, device=q.device)
-        binding.dfa_attn_block_fwd(q, k, v, blk, op, lp, scale=scale, stream=stream)
+        binding.dfa_attn_block_fwd(q, k, v, blk, op, lp, scale=scale, stream=stream, docs=docs)
         for r in range(repeats):
             ev[2 * r].record(stream)
-            binding.dfa_attn_block_fwd(q, k, v, blk, op, lp, scale=scale, stream=stream)
+            binding.dfa_attn_block_fwd(q, k, v, blk, op, lp, scale=scale, stream=stream, docs=docs)
             ev[2 * r + 1].record(stream)
         stream.synchronize()
         times[rank, step] += float(np.median([ev[2 * r].elapsed_time(ev[2 * r + 1])
@@ -58,11 +60,34 @@ def measured_balance(times) -> dict:
             "busy": busy, "bubble": bubble}
 
 
-def pair_times(blocks, n_ranks: int):
+def pair_times(blocks, n_ranks: int, pairs=None):
     """The pair counts of the block list in the same [rank, step] layout (the
-    cost model in which dfa_schedule_balance measures the bubble)."""
+    cost model in which dfa_schedule_balance measures the bubble); ``pairs``
+    overrides the blocks' own counts (e.g. doc_pair_counts)."""
     arr = binding._blocks_arg(blocks)
     t = np.zeros((n_ranks, n_ranks), dtype=np.float64)
-    for blk in arr:
-        t[int(blk[0]), int(blk[1])] += float(blk[9])
+    for n, blk in enumerate(arr):
+        t[int(blk[0]), int(blk[1])] += float(blk[9] if pairs is None else pairs[n])
     return t
+
+
+def _piece_positions(start, length, stride, run):
+    i = np.arange(length, dtype=np.int64)
+    return start + (i // run) * stride + i % run
+
+
+def doc_pair_counts(blocks, bounds):
+    """Visible pairs of each block when the sequence packs documents with
+    cumulative boundaries ``bounds`` (host array): pairs (query, key) with the
+    key not after the query and both in one document (Striped Attention Guide,
+    "Production Deployment and Best Practices", item 3)."""
+    arr = binding._blocks_arg(blocks)
+    b = np.asarray(bounds, dtype=np.int64).reshape(-1)
+    out = np.zeros(len(arr), dtype=np.int64)
+    for n, blk in enumerate(arr):
+        qp = _piece_positions(blk[3], blk[5], blk[7], blk[10])
+        kp = _piece_positions(blk[4], blk[6], blk[7], blk[10])
+        lo = b[np.searchsorted(b, qp, side="right") - 1]
+        seen = np.searchsorted(kp, qp, side="right") - np.searchsorted(kp, lo, side="left")
+        out[n] = int(np.maximum(seen, 0).sum())
+    return out

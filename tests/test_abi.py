@@ -41,9 +41,10 @@ def test_struct_layout_matches_header(bd, tmp_path):
 #include <stddef.h>
 #include "{HEADER}"
 int main(void) {{
-  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(dfa_block), sizeof(dfa_attn_desc),
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(dfa_block), sizeof(dfa_attn_desc),
          offsetof(dfa_attn_desc, seqlen), offsetof(dfa_attn_desc, q_strides),
          offsetof(dfa_attn_desc, o_strides), offsetof(dfa_attn_desc, softmax_scale),
+         offsetof(dfa_attn_desc, doc_bounds), offsetof(dfa_attn_desc, n_docs),
          sizeof(dfa_balance), offsetof(dfa_balance, bubble), sizeof(dfa_kernel_marks),
          offsetof(dfa_kernel_marks, dv_begin));
   return 0;
@@ -54,6 +55,7 @@ int main(void) {{
     D = bd.DfaAttnDesc
     assert vals == [ctypes.sizeof(bd.DfaBlock), ctypes.sizeof(D), D.seqlen.offset,
                     D.q_strides.offset, D.o_strides.offset, D.softmax_scale.offset,
+                    D.doc_bounds.offset, D.n_docs.offset,
                     ctypes.sizeof(bd.DfaBalance), bd.DfaBalance.bubble.offset,
                     ctypes.sizeof(bd.DfaKernelMarks), bd.DfaKernelMarks.dv_begin.offset]
     assert vals[0] == 88
@@ -96,6 +98,13 @@ def test_workspace_size_and_descriptor_validation(bd):
     assert ws_size(bd, desc(bd, head_dim=96), blocks, 0)[0] == bd.DFA_E_UNSUPPORTED
     assert ws_size(bd, desc(bd, dtype=5), blocks, 0)[0] == bd.DFA_E_UNSUPPORTED
     assert ws_size(bd, desc(bd, heads_kv=3), blocks, 0)[0] == bd.DFA_E_SHAPE
+    # packed documents: 1 <= n_docs <= seqlen (the bounds themselves live on
+    # the device and are never read by the host)
+    fake = ctypes.c_void_p(0x1000)
+    assert ws_size(bd, desc(bd, doc_bounds=fake, n_docs=3), blocks, 0)[0] == 0
+    assert ws_size(bd, desc(bd, doc_bounds=fake, n_docs=0), blocks, 0)[0] == bd.DFA_E_SHAPE
+    assert ws_size(bd, desc(bd, doc_bounds=fake, n_docs=257), blocks, 0)[0] == bd.DFA_E_SHAPE
+    assert ws_size(bd, desc(bd, n_docs=-5), blocks, 0)[0] == 0  # ignored without bounds
     d = desc(bd)
     d.q_strides[1] = 4 * 128 + 4  # not a multiple of 16 bytes
     assert ws_size(bd, d, blocks, 0)[0] == bd.DFA_E_ALIGN

@@ -131,16 +131,18 @@ def test_stripe_block_parity(dfa, case, dtype):
     check_schedule(dfa, blocks, 4000 + N + P, N, B, Hq, Hkv, D, dtype)
 
 
-def check_schedule(dfa, blocks, seed, N, B, Hq, Hkv, D, dtype):
+def check_schedule(dfa, blocks, seed, N, B, Hq, Hkv, D, dtype, docs=None):
     """Fused and stepwise forward and the backward of a block list against the
-    oracle on the rows it touches; every other row must come out zero."""
+    oracle on the rows it touches; every other row must come out zero.
+    ``docs``: optional cumulative document boundaries (packed documents)."""
     (q, k, v, do), (tq, tk, tv, tdo) = make(seed, B, N, Hq, Hkv, D, dtype)
     scale = 1 / np.sqrt(D)
+    td = None if docs is None else torch.tensor(docs, dtype=torch.int32, device="cuda")
     rows, krows = rows_of(blocks), kv_rows_of(blocks)
-    ro, rl = oracle.attn_rows(q, k, v, scale, rows=rows)
+    ro, rl = oracle.attn_rows(q, k, v, scale, rows=rows, docs=docs)
     outs = {}
     for mode in (dfa.DFA_FWD_FUSED, dfa.DFA_FWD_STEPWISE):
-        o, lse = dfa.dfa_attn_fwd(tq, tk, tv, blocks, mode)
+        o, lse = dfa.dfa_attn_fwd(tq, tk, tv, blocks, mode, docs=td)
         torch.cuda.synchronize()
         go, gl = bhnd(to_np(o)), to_np(lse)
         check_out(go[:, :, rows], ro, gl[:, :, rows], rl, dtype, f"mode {mode}")
@@ -148,9 +150,10 @@ def check_schedule(dfa, blocks, seed, N, B, Hq, Hkv, D, dtype):
         assert np.all(go[:, :, other] == 0) and np.all(np.isneginf(gl[:, :, other]))
         outs[mode] = (o, lse)
     o, lse = outs[dfa.DFA_FWD_FUSED]
-    dq, dk, dv = dfa.dfa_attn_bwd(tq, tk, tv, o, tdo, lse, blocks)
+    dq, dk, dv = dfa.dfa_attn_bwd(tq, tk, tv, o, tdo, lse, blocks, docs=td)
     torch.cuda.synchronize()
-    (rdq, rdk, rdv), (adq, adk, adv) = oracle.attn_grads(q, k, v, do, scale, rows=rows, with_abs=True)
+    (rdq, rdk, rdv), (adq, adk, adv) = oracle.attn_grads(q, k, v, do, scale, rows=rows, with_abs=True,
+                                                          docs=docs)
     gq, gk, gv = bhnd(to_np(dq)), bhnd(to_np(dk)), bhnd(to_np(dv))
     check_grad(gq[:, :, rows], rdq, adq, dtype, "dq")
     check_grad(gk[:, :, krows], rdk[:, :, krows], adk[:, :, krows], dtype, "dk")
@@ -158,6 +161,47 @@ def check_schedule(dfa, blocks, seed, N, B, Hq, Hkv, D, dtype):
     # rows no block touches are zero, including key rows of other ranks
     for g, touched in ((gq, rows), (gk, krows), (gv, krows)):
         assert np.all(g[:, :, np.setdiff1d(np.arange(N), touched)] == 0)
+
+
+# packed documents (the striped-attention page's document-packing practice):
+# schedule kind, N, P, stripe, batch, Hq, Hkv, d, subset rank, document lengths
+DOC_CASES = [
+    (BAL, 2048, 4, 1, 1, 2, 1, 128, None, (1, 700)),
+    (RING, 1024, 4, 1, 2, 2, 2, 64, None, (64, 64)),      # boundaries on tile edges
+    (RING, 1024, 4, 1, 1, 2, 2, 128, None, (63, 65)),     # boundaries next to tile edges
+    (STR, 1024, 8, 1, 1, 4, 2, 128, None, (1, 300)),
+    (sr.STRIPED_BLOCK, 2048, 4, 64, 1, 2, 2, 128, None, (100, 900)),
+    (BAL, 2048, 8, 1, 1, 2, 1, 128, 3, (1, 500)),          # one folded rank's share
+    (BAL, 512, 2, 1, 1, 2, 2, 128, None, (1, 1)),         # every token its own document
+    (BAL, 1000, 4, 1, 2, 2, 2, 128, None, (1000, 1000)),  # one document: plain causal
+]
+
+
+@pytest.mark.parametrize("case", DOC_CASES, ids=lambda c: "-".join(str(x) for x in c))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_document_mask_parity(dfa, case, dtype):
+    from long_context_sequence_dfa_amd import inputs
+    kind, N, P, stripe, B, Hq, Hkv, D, sub, (lmin, lmax) = case
+    if dtype == "f32" and (N > 1024 or Hq > 2):
+        pytest.skip("fp32 path covered on the smaller cases")
+    docs = inputs.doc_bounds(5000 + N + P, N, lmin, lmax)
+    say(f"case: documents {sr.KIND_NAMES[kind]} N={N} P={P} stripe={stripe} B={B} Hq={Hq} "
+        f"Hkv={Hkv} D={D} rank={sub} docs={len(docs) - 1} {dtype}")
+    if kind == sr.STRIPED_BLOCK:
+        blocks = dfa.dfa_schedule_build_striped_blocks(N, P, stripe)
+    else:
+        blocks = dfa.dfa_schedule_build(kind, N, P)
+    if sub is not None:
+        blocks = blocks[blocks[:, 0] == sub]
+    seed = 5000 + N + P
+    (q, k, v, _), (tq, tk, tv, _) = make(seed, B, N, Hq, Hkv, D, dtype)
+    td = torch.tensor(docs, dtype=torch.int32, device="cuda")
+    for b in blocks[:4]:  # single-block partials under the document mask
+        op, lp = dfa.dfa_attn_block_fwd(tq, tk, tv, b, docs=td)
+        torch.cuda.synchronize()
+        xo, xl = oracle.block_partial(q, k, v, 1 / np.sqrt(D), *b[3:8], run=b[10], docs=docs)
+        check_out(to_np(op), xo, to_np(lp), xl, dtype, f"block {b[:3]}")
+    check_schedule(dfa, blocks, seed, N, B, Hq, Hkv, D, dtype, docs=docs)
 
 
 def test_block_partials_bf16_with_empty_rows(dfa):

@@ -23,8 +23,11 @@ WORKLOADS = {
     "gqa-32-8-n256k-balanced-p32": (262144, 32, 8, sr.BALANCED, 32, 1005, False, None, [1]),
     # stripe blocks of 64 tokens at the Llama-7B shape (kind STRIPED_BLOCK)
     "llama7b-n32k-striped64-p8": (32768, 32, 32, sr.STRIPED_BLOCK, 8, 1003, True, None, [9]),
+    # packed documents of 1K-8K tokens over the folded schedule
+    "llama7b-n32k-docs-balanced-p8": (32768, 32, 32, sr.BALANCED, 8, 1003, True, None, [4]),
 }
 STRIPE = {"llama7b-n32k-striped64-p8": 64}
+DOCS = {"llama7b-n32k-docs-balanced-p8": (1024, 8192)}
 
 
 @pytest.fixture(scope="module")
@@ -53,9 +56,11 @@ def test_workload_sampled_parity(dfa, name):
         blocks = dfa.dfa_schedule_build(kind, N, P)
     if rank is not None:
         blocks = blocks[blocks[:, 0] == rank]
+    docs = inputs.doc_bounds(seed, N, *DOCS[name]) if name in DOCS else None
+    td = None if docs is None else torch.tensor(docs, dtype=torch.int32, device=dev)
     print(f"case: {name} forward + backward on the GPU ({len(blocks)} blocks)", flush=True)
-    o, lse = dfa.dfa_attn_fwd(tq, tk, tv, blocks)
-    dq, dk, dv = dfa.dfa_attn_bwd(tq, tk, tv, o, tdo, lse, blocks)
+    o, lse = dfa.dfa_attn_fwd(tq, tk, tv, blocks, docs=td)
+    dq, dk, dv = dfa.dfa_attn_bwd(tq, tk, tv, o, tdo, lse, blocks, docs=td)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all() and torch.isfinite(dq.float()).all()
     assert torch.isfinite(dk.float()).all() and torch.isfinite(dv.float()).all()
@@ -64,8 +69,11 @@ def test_workload_sampled_parity(dfa, name):
     rng = np.random.default_rng(seed)
     chunk = {sr.BALANCED: N // (2 * P), sr.STRIPED_BLOCK: STRIPE.get(name, 1)}.get(kind, N // P)
     edges = [x for c in range(1, N // chunk) for x in (c * chunk - 1, c * chunk)]
+    if docs is not None:  # both sides of every document boundary
+        edges += [x for b in docs[1:-1] for x in (b - 1, b)]
     cand = np.concatenate([rng.choice(rows_all, 40, replace=False), rows_all[:4], rows_all[-4:],
-                           np.array(edges[:8] + edges[-8:], dtype=np.int64)])
+                           np.array(edges[:8] + edges[-8:], dtype=np.int64)]
+                          + ([] if docs is None else [np.array(edges[-2 * (len(docs) - 2):], dtype=np.int64)]))
     rows = np.intersect1d(np.unique(cand), rows_all)
     scale = 1 / math.sqrt(D)
     for hk in kv_heads:
@@ -73,20 +81,22 @@ def test_workload_sampled_parity(dfa, name):
         print(f"case: {name} oracle, kv head {hk}, {rows.size} rows", flush=True)
         qh, doh = q[:, :, heads], do[:, :, heads]
         kh, vh = k[:, :, [hk]], v[:, :, [hk]]
-        ro, rl = oracle.attn_rows(qh, kh, vh, scale, rows=rows)
+        ro, rl = oracle.attn_rows(qh, kh, vh, scale, rows=rows, docs=docs)
         go = bhnd(to_np(o[:, rows][:, :, heads]))
         gl = to_np(lse[:, heads][:, :, rows])
         check_out(go, ro, gl, rl, "bf16", f"{name} O")
-        lse_r, dd_r, rdq, aa, adq = oracle.grad_rows(qh, kh, vh, doh, scale, rows=rows, with_abs=True)
+        lse_r, dd_r, rdq, aa, adq = oracle.grad_rows(qh, kh, vh, doh, scale, rows=rows, with_abs=True,
+                                                     docs=docs)
         gq = bhnd(to_np(dq[:, rows][:, :, heads]))
         # the rms of a sampled gradient set stands in for the tensor's
         check_grad(gq, rdq, adq, "bf16", f"{name} dQ", check_mean=False)
         # last key rows: their query rows are the tail of the row set
         tail_rows = rows_all[rows_all >= N - 96]
         keys = np.arange(N - 64, N)
-        l2, d2, _, a2, _ = oracle.grad_rows(qh, kh, vh, doh, scale, rows=tail_rows, with_abs=True)
+        l2, d2, _, a2, _ = oracle.grad_rows(qh, kh, vh, doh, scale, rows=tail_rows, with_abs=True,
+                                            docs=docs)
         rdk, rdv, adk, adv = oracle.grad_cols(qh, kh, vh, doh, scale, tail_rows, l2, d2, keys=keys,
-                                              aa=a2)
+                                              aa=a2, docs=docs)
         gk = bhnd(to_np(dk[:, keys][:, :, [hk]]))
         gv = bhnd(to_np(dv[:, keys][:, :, [hk]]))
         check_grad(gk, rdk, adk, "bf16", f"{name} dK", check_mean=False)

@@ -51,3 +51,27 @@ def test_measured_bubbles_of_the_three_schedules():
     assert out[0] > 0.3
     assert out[1] < 0.2 and out[2] < 0.2
     assert out[0] > 2 * max(out[1], out[2])
+
+
+@pytest.mark.parametrize("kind,N,P,stripe", [(0, 64, 4, 1), (1, 96, 3, 1), (2, 64, 8, 1), (3, 128, 2, 8)])
+def test_doc_pair_counts(kind, N, P, stripe):
+    """Visible pairs per block under packed documents: with one document they
+    are the blocks' own counts; summed over a schedule they are the causal
+    pairs inside each document, L (L + 1) / 2 per document of length L; and
+    each block agrees with a brute-force count over its positions."""
+    from long_context_sequence_dfa_amd import binding as bd, inputs
+    from oracle import schedule_ref as sr
+    blocks = (bd.dfa_schedule_build_striped_blocks(N, P, stripe) if kind == 3
+              else bd.dfa_schedule_build(kind, N, P))
+    one = timeline.doc_pair_counts(blocks, [0, N])
+    assert np.array_equal(one, blocks[:, 9])
+    docs = inputs.doc_bounds(77, N, 1, 20)
+    cnt = timeline.doc_pair_counts(blocks, docs)
+    lens = np.diff(docs)
+    assert cnt.sum() == int((lens * (lens + 1) // 2).sum())
+    did = np.searchsorted(docs, np.arange(N), side="right") - 1
+    for blk, c in zip(blocks, cnt):
+        qp = sr.positions((blk[3], blk[5], blk[7], blk[10]))
+        kp = sr.positions((blk[4], blk[6], blk[7], blk[10]))
+        brute = sum(1 for i in qp for j in kp if j <= i and did[i] == did[j])
+        assert c == brute
