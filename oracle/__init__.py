@@ -7,6 +7,7 @@ in ``long_context_sequence_dfa_amd`` and the library never calls it.
 * ``oracle.c`` (compiled here with gcc + OpenMP) holds the attention maths:
   full causal attention rows (O1), one block's partial result (O2), the merge
   of partials (O3) and the two halves of the gradient (O5).
+  It also holds the rotary position embedding at absolute positions (O6).
 * ``schedule_ref.py`` enumerates the virtual-rank schedules by brute force.
 
 Every array argument is float64; inputs are the exact stored values of the
@@ -53,8 +54,9 @@ def _load():
             lib.orc_grad_rows.argtypes = [i64] * 5 + [f64] + [p] * 4 + [i64, p, i64, p] + [p] * 6
             lib.orc_grad_cols.argtypes = ([i64] * 5 + [f64] + [p] * 4 + [i64, p, p, p]
                                           + [i64, p, i64, p, p, p, p, p, p, p])
+            lib.orc_rope.argtypes = [i64] * 4 + [p, p, i64, f64, ctypes.c_int]
             for f in ("orc_attn_rows", "orc_block_partial", "orc_merge", "orc_grad_rows",
-                      "orc_grad_cols", "orc_num_threads"):
+                      "orc_grad_cols", "orc_num_threads", "orc_rope"):
                 getattr(lib, f).restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -234,3 +236,24 @@ def attn_grads(q, k, v, dout, scale, rows=None, with_abs=False, docs=None):
     lse, dd, dq, aa, dq_abs = grad_rows(q, k, v, dout, scale, rows=rows, with_abs=True, docs=docs)
     dk, dv, dk_abs, dv_abs = grad_cols(q, k, v, dout, scale, rows, lse, dd, aa=aa, docs=docs)
     return (dq, dk, dv), (dq_abs, dk_abs, dv_abs)
+
+
+def rope(x, base=10000.0, pos_offset=0, inverse=False):
+    """O6: rotary position embedding of x [B, N, H, d] at positions
+    pos_offset + token index (interleaved pairs, angle pos * base^(-2c/d));
+    ``inverse`` rotates back.  Returns float64 [B, N, H, d]."""
+    x = _f64(x)
+    B, N, H, d = x.shape
+    y = np.zeros_like(x)
+    _check(_load().orc_rope(B, N, H, d, _ptr(x), _ptr(y), int(pos_offset), float(base),
+                            1 if inverse else 0), "rope")
+    return y
+
+
+def round_bf16(x):
+    """float64 -> nearest fp32 -> nearest-even bf16, returned as float64 (the
+    storage rounding of a bf16 tensor written from an fp32 value)."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64)).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)

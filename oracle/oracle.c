@@ -416,6 +416,39 @@ int orc_grad_cols(int64_t B, int64_t N, int64_t Hq, int64_t Hkv, int64_t d, doub
   return ORC_OK;
 }
 
+/*
+ * O6 -- rotary position embedding at absolute positions (Striped Attention
+ * Guide, "Preserving Rotary Position Embeddings (RoPE)": each token vector is
+ * rotated by its absolute sequence index, q_rot = R(Theta, i) q).  The pages
+ * name the rotation but not its parameters; this is the RoFormer form with
+ * interleaved pairs: pair c = (x[2c], x[2c+1]) turns by the angle
+ * pos * base^(-2c/d), pos = pos_offset + token index.  inverse != 0 turns by
+ * minus that angle (the transpose, used for gradients).
+ *   x, y : [B][N][H][d] contiguous (y may equal x)
+ */
+int orc_rope(int64_t B, int64_t N, int64_t H, int64_t d, const double *x, double *y,
+             int64_t pos_offset, double base, int inverse) {
+  if (B < 1 || N < 0 || H < 1 || d < 2 || d % 2 || base <= 0.0) return ORC_EARG;
+  double sgn = inverse ? -1.0 : 1.0;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < N; ++t) {
+    double pos = (double)(pos_offset + t);
+    for (int64_t c = 0; c < d / 2; ++c) {
+      double theta = pos * pow(base, -2.0 * (double)c / (double)d);
+      double cs = cos(theta), sn = sgn * sin(theta);
+      for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < H; ++h) {
+          const double *xi = x + ((b * N + t) * H + h) * d;
+          double *yi = y + ((b * N + t) * H + h) * d;
+          double a0 = xi[2 * c], a1 = xi[2 * c + 1];
+          yi[2 * c] = a0 * cs - a1 * sn;
+          yi[2 * c + 1] = a0 * sn + a1 * cs;
+        }
+    }
+  }
+  return ORC_OK;
+}
+
 /* Number of OpenMP threads a parallel region of this library uses. */
 int orc_num_threads(void) {
   int n = 1;

@@ -336,3 +336,54 @@ def test_document_bounds_are_validated(orc):
     for bad in ([0, 3], [1, 5], [0, 3, 3, 5], [0, 4, 2, 5]):
         with pytest.raises(ValueError):
             orc.attn_rows(q, q, q, 1.0, docs=bad)
+
+
+# ---------------------------------------------------------------------------
+# Rotary position embedding at absolute positions (Striped Attention Guide,
+# "Preserving Rotary Position Embeddings (RoPE)").
+
+
+def test_rope_single_pair_closed_form(orc):
+    """d = 2: one pair turning by pos radians (frequency base^0 = 1)."""
+    x = rand(1, 7, 1, 2)
+    y = orc.rope(x, base=10000.0)
+    p = np.arange(7)
+    np.testing.assert_allclose(y[0, :, 0, 0], x[0, :, 0, 0] * np.cos(p) - x[0, :, 0, 1] * np.sin(p), atol=1e-15)
+    np.testing.assert_allclose(y[0, :, 0, 1], x[0, :, 0, 0] * np.sin(p) + x[0, :, 0, 1] * np.cos(p), atol=1e-15)
+
+
+def test_rope_frequencies_and_offset(orc):
+    """d = 4, base b: pair 1 turns by pos / sqrt(b); pos_offset shifts positions."""
+    x = np.zeros((1, 3, 1, 4))
+    x[..., 2] = 1.0  # unit vector in pair 1
+    y = orc.rope(x, base=100.0, pos_offset=5)
+    ang = (5 + np.arange(3)) / 10.0
+    np.testing.assert_allclose(y[0, :, 0, 2], np.cos(ang), atol=1e-15)
+    np.testing.assert_allclose(y[0, :, 0, 3], np.sin(ang), atol=1e-15)
+    assert np.all(y[..., :2] == 0)
+
+
+def test_rope_identity_norms_inverse_relative(orc):
+    B, N, H, d = 2, 40, 3, 16
+    x = rand(B, N, H, d)
+    y = orc.rope(x)
+    np.testing.assert_allclose(y[:, 0], x[:, 0], atol=0)  # position 0: no rotation
+    pn = lambda a: np.sqrt(a[..., 0::2] ** 2 + a[..., 1::2] ** 2)
+    np.testing.assert_allclose(pn(y), pn(x), atol=1e-13)   # each pair keeps its length
+    np.testing.assert_allclose(orc.rope(y, inverse=True), x, atol=1e-13)
+    # the score depends on the distance only: positions (i, j) and (i + s, j + s)
+    q, k = rand(1, 1, 1, d), rand(1, 1, 1, d)
+    for i, j, sft in ((9, 4, 17), (30, 30, 5), (3, 11, 1000)):
+        a = np.sum(orc.rope(q, pos_offset=i) * orc.rope(k, pos_offset=j))
+        b = np.sum(orc.rope(q, pos_offset=i + sft) * orc.rope(k, pos_offset=j + sft))
+        assert abs(a - b) < 1e-11
+
+
+def test_round_bf16_nearest_even(orc):
+    v = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, -2.5 - 2 ** -9, 3.0e38, 1e-40])
+    r = orc.round_bf16(v)
+    assert list(r[:3]) == [1.0, 1.0, 1.0 + 2 ** -6]
+    assert r[3] == -2.5
+    assert np.all(np.isfinite(r[:4]))
+    t = torch.tensor(v, dtype=torch.float32).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(r, t)
