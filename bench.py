@@ -55,6 +55,11 @@ WORKLOADS = {
     "llama7b-n32k-docs-striped64-p8": dict(B=1, N=32768, Hq=32, Hkv=32, D=128, kind=2, P=8,
                                            seed=1003, scaled=True, rank=None, stripe=64,
                                            docs=(1024, 8192)),
+    # rotary embedding of q and k at absolute positions before the ring (the
+    # striped-attention page's RoPE placement), gradients turned back after it
+    "llama7b-n32k-rope-striped64-p8": dict(B=1, N=32768, Hq=32, Hkv=32, D=128, kind=2, P=8,
+                                           seed=1003, scaled=True, rank=None, stripe=64,
+                                           rope=10000.0),
 }
 
 
@@ -234,18 +239,33 @@ def main() -> int:
     sp = ctypes.c_void_p(stream.cuda_stream)
     ev = HipEvents()
     # per step: fwd begin, fwd end, then the backward's marks
-    ev_all = [[ev.create() for _ in range(7)] for _ in range(args.steps)]
+    ev_all = [[ev.create() for _ in range(9)] for _ in range(args.steps)]
+    rope = wl.get("rope")
+    qr, kr = (torch.empty_like(tq), torch.empty_like(tk)) if rope else (tq, tk)
 
     def step(m=None):
+        # events: 7 forward begin (rotation of q, k first), 0 attention
+        # forward begin, 1 forward end, 2-6 backward marks, 8 after the
+        # gradients are turned back (rotations only: 7 == 0, 8 == 6)
+        if m is not None:
+            ev.h.hipEventRecord(m[7], sp)
+        if rope:
+            dfa.dfa_rope(tq, qr, base=rope)
+            dfa.dfa_rope(tk, kr, base=rope)
         if m is not None:
             ev.h.hipEventRecord(m[0], sp)
-        dfa.dfa_attn_fwd(tq, tk, tv, blocks, mode, o=o, lse=lse, workspace=ws_f, docs=td)
+        dfa.dfa_attn_fwd(qr, kr, tv, blocks, mode, o=o, lse=lse, workspace=ws_f, docs=td)
         marks = None
         if m is not None:
             ev.h.hipEventRecord(m[1], sp)
             marks = binding.DfaKernelMarks(m[2], m[3], m[4], m[5], m[6])
-        dfa.dfa_attn_bwd(tq, tk, tv, o, tdo, lse, blocks, dq=dq, dk=dk, dv=dv, workspace=ws_b,
+        dfa.dfa_attn_bwd(qr, kr, tv, o, tdo, lse, blocks, dq=dq, dk=dk, dv=dv, workspace=ws_b,
                          marks=marks, docs=td)
+        if rope:
+            dfa.dfa_rope(dq, dq, base=rope, inverse=True)
+            dfa.dfa_rope(dk, dk, base=rope, inverse=True)
+        if m is not None:
+            ev.h.hipEventRecord(m[8], sp)
 
     if args.calibrate_copy:
         # one plain device copy of known size: the scale for HBM byte counters
@@ -288,7 +308,7 @@ def main() -> int:
 
     per = {name: float(np.mean([ev.elapsed(m[a], m[b]) for m in ev_all]))
            for name, a, b in (("fwd", 0, 1), ("bwd", 1, 6), ("bwd_pre", 2, 3), ("dq", 3, 4),
-                              ("dk", 4, 5), ("dv", 5, 6))}
+                              ("dk", 4, 5), ("dv", 5, 6), ("rope_in", 7, 0), ("rope_back", 6, 8))}
     ms_step = elapsed * 1e3 / args.steps
     total_flops = (fwd_flops + bwd_flops) * args.steps
     value = total_flops / elapsed / 1e12
@@ -324,6 +344,10 @@ def main() -> int:
         "fwd_ms": fwd_avg,
         "bwd_ms": bwd_avg,
         "kernel_ms": {k_: per[k_] for k_ in ("fwd", "bwd_pre", "dq", "dk", "dv")},
+        **({"rope_ms": {"q_k_forward": per["rope_in"], "dq_dk_back": per["rope_back"]},
+            # q and k forward, dq and dk back: each pass reads and writes its bf16 tensor once
+            "rope_gbs": 8.0 * (tq.numel() + tk.numel()) / ((per["rope_in"] + per["rope_back"]) * 1e-3) / 1e9}
+           if rope else {}),
         "fwd_tflops": fwd_flops / (fwd_avg * 1e-3) / 1e12,
         f"fwd_{'stepwise' if mode == dfa.DFA_FWD_FUSED else 'fused'}_ms": alt_ms,
         f"fwd_{'stepwise' if mode == dfa.DFA_FWD_FUSED else 'fused'}_tflops": fwd_flops / (alt_ms * 1e-3) / 1e12,
@@ -337,6 +361,7 @@ def main() -> int:
                    "stripe": wl.get("stripe", 1),
                    "documents": None if docs is None else {"count": len(docs) - 1,
                                                             "lengths": list(wl["docs"])},
+                   "rope_base": rope,
                    "virtual_ranks": wl["P"], "rank_share": wl["rank"], "mode": args.mode,
                    "parallelism": "none: virtual ranks on one GPU"},
         "roofline": roofline,

@@ -308,6 +308,33 @@ dfa_status dfa_attn_bwd_ex(const dfa_attn_desc *d, const dfa_block *blocks, int6
 dfa_status dfa_workspace_size(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n_blocks,
                               int32_t op, size_t *bytes);
 
+/*
+ * dfa_rope -- rotary position embedding at absolute positions (Striped
+ * Attention Guide, "Preserving Rotary Position Embeddings (RoPE)": each token
+ * vector turns by its absolute sequence index, applied before the ring
+ * exchange).  The pages name the rotation without its parameters; this is
+ * the RoFormer form with interleaved pairs: pair c = (x[2c], x[2c+1]) of the
+ * token with index t turns by (pos_offset + t) * base^(-2c/head_dim)
+ * (base 10000 in the usual models).  inverse = 1 turns by minus that angle:
+ * the transpose, which maps gradients of the rotated tensor back
+ * (dq = dfa_rope(dq_rot, inverse = 1)).  Tensors of this library hold global
+ * token order, so a striped shard's row m of rank p already sits at its
+ * absolute position m*P + p.
+ *   dtype          : DFA_BF16 or DFA_F32 (x and y alike).
+ *   x, y           : device [batch][seqlen][heads][head_dim], element strides
+ *                    x_strides / y_strides (batch, token, head; host arrays of
+ *                    3), head_dim contiguous.  y == x (same strides) rotates in
+ *                    place; other overlaps are not allowed.
+ *   head_dim       : even, 2..512.  Strides even; x and y aligned to one pair
+ *                    (4 bytes bf16, 8 bytes fp32), else DFA_E_ALIGN.
+ *   pos_offset     : position of token 0 (>= 0).
+ * The angle and its sine and cosine are computed in fp64; each output is
+ * rounded once (to fp32, then for bf16 to bf16, nearest even).
+ */
+dfa_status dfa_rope(int32_t dtype, int32_t batch, int64_t seqlen, int32_t heads, int32_t head_dim,
+                    const int64_t *x_strides, const void *x, const int64_t *y_strides, void *y,
+                    int64_t pos_offset, double base, int32_t inverse, void *stream);
+
 /* Static English text for a status code (never NULL). */
 const char *dfa_status_string(dfa_status s);
 

@@ -27,7 +27,7 @@ DFA_OP_FWD_FUSED, DFA_OP_FWD_STEPWISE, DFA_OP_BWD = 0, 1, 2
 EXPORTED = ("dfa_schedule_build", "dfa_schedule_build_striped_blocks", "dfa_schedule_balance",
             "dfa_attn_block_fwd", "dfa_lse_merge",
             "dfa_attn_fwd", "dfa_attn_bwd", "dfa_attn_bwd_ex", "dfa_workspace_size",
-            "dfa_status_string")
+            "dfa_rope", "dfa_status_string")
 BLOCK_FIELDS = ("rank", "step", "kv_rank", "q_start", "kv_start", "len_q", "len_kv", "stride",
                 "diag_offset", "pairs", "run")
 NB = len(BLOCK_FIELDS)
@@ -87,6 +87,7 @@ def lib() -> ctypes.CDLL:
             L.dfa_attn_bwd.argtypes = [p, p, i64, p, p, p, p, p, p, p, p, p, p, sz, p]
             L.dfa_attn_bwd_ex.argtypes = [p, p, i64, p, p, p, p, p, p, p, p, p, p, sz, p, p]
             L.dfa_workspace_size.argtypes = [p, p, i64, i32, ctypes.POINTER(sz)]
+            L.dfa_rope.argtypes = [i32, i32, i64, i32, i32, p, p, p, p, i64, ctypes.c_double, i32, p]
             L.dfa_status_string.argtypes = [i32]
             L.dfa_status_string.restype = ctypes.c_char_p
             for f in EXPORTED[:-1]:
@@ -256,6 +257,24 @@ def dfa_lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):
     _check(lib().dfa_lse_merge(n_rows, D, _ptr(o_acc), _ptr(lse_acc), _ptr(o_part),
                                _ptr(lse_part), _stream(stream)), "dfa_lse_merge")
     return o_acc, lse_acc
+
+
+def dfa_rope(x, y=None, pos_offset=0, base=10000.0, inverse=False, stream=None):
+    """Rotary position embedding of x [B, N, H, d] (bf16 or fp32) at absolute
+    positions pos_offset + token index; ``inverse`` turns back.  Writes y
+    (default: a new tensor like x; pass y=x to rotate in place)."""
+    import torch
+    if x.dim() != 4 or x.stride(3) != 1:
+        raise ValueError("x must be [B, N, H, d] with d contiguous")
+    y = torch.empty_like(x) if y is None else y
+    if y.shape != x.shape or y.dtype != x.dtype or y.stride(3) != 1:
+        raise ValueError("y must match x")
+    B, N, H, D = x.shape
+    xs = (ctypes.c_int64 * 3)(*x.stride()[:3])
+    ys = (ctypes.c_int64 * 3)(*y.stride()[:3])
+    _check(lib().dfa_rope(_dtype_code(x), B, N, H, D, xs, _ptr(x), ys, _ptr(y), int(pos_offset),
+                          float(base), 1 if inverse else 0, _stream(stream)), "dfa_rope")
+    return y
 
 
 def dfa_attn_fwd(q, k, v, blocks, mode=DFA_FWD_FUSED, o=None, lse=None, workspace=None,

@@ -451,7 +451,44 @@ dfa_status check_ws(void *ws, size_t have, size_t need) {
 
 }  // namespace
 
-extern "C" const char *dfa_status_string(dfa_status s) {
+extern "C" dfa_status dfa_rope(int32_t dtype, int32_t batch, int64_t seqlen, int32_t heads, int32_t head_dim,
+                    const int64_t *x_strides, const void *x, const int64_t *y_strides, void *y,
+                    int64_t pos_offset, double base, int32_t inverse, void *stream) {
+  if (!x_strides || !y_strides) return DFA_E_NULL;
+  if (dtype != DFA_BF16 && dtype != DFA_F32) return DFA_E_UNSUPPORTED;
+  if (head_dim < 2 || head_dim > 512 || head_dim % 2) return DFA_E_UNSUPPORTED;
+  if (batch < 1 || heads < 1 || seqlen < 0 || pos_offset < 0) return DFA_E_SHAPE;
+  if (!(base > 0.0) || !std::isfinite(base) || (inverse != 0 && inverse != 1)) return DFA_E_SHAPE;
+  if (seqlen == 0) return DFA_OK;
+  if (!x || !y) return DFA_E_NULL;
+  const uintptr_t pair = dtype == DFA_BF16 ? 4 : 8;
+  if ((reinterpret_cast<uintptr_t>(x) % pair) || (reinterpret_cast<uintptr_t>(y) % pair))
+    return DFA_E_ALIGN;
+  bool same = true;
+  for (int i = 0; i < 3; ++i) {
+    if (x_strides[i] < 0 || y_strides[i] < 0) return DFA_E_SHAPE;
+    if ((x_strides[i] % 2) || (y_strides[i] % 2)) return DFA_E_ALIGN;
+    same = same && x_strides[i] == y_strides[i];
+  }
+  if (x == y && !same) return DFA_E_SHAPE;
+  dfa::RopeArgs a{};
+  a.x = x;
+  a.y = y;
+  for (int i = 0; i < 3; ++i) {
+    a.xs[i] = x_strides[i];
+    a.ys[i] = y_strides[i];
+  }
+  a.seqlen = seqlen;
+  a.pos_offset = pos_offset;
+  a.base = base;
+  a.batch = batch;
+  a.heads = heads;
+  a.head_dim = head_dim;
+  a.inverse = inverse;
+  return hip_status(dfa::launch_rope(a, dtype == DFA_BF16, static_cast<hipStream_t>(stream)));
+}
+
+const char *dfa_status_string(dfa_status s) {
   switch (s) {
     case DFA_OK: return "ok";
     case DFA_E_NULL: return "a required pointer is NULL";

@@ -144,6 +144,17 @@ constexpr int kBwdTileKV = 32 * kBwdWaves;  // bf16 dk/dv: key rows per workgrou
 constexpr int kF32TileQ = 64;    // fp32 kernels: rows per workgroup
 constexpr int kF32TileKV = 64;
 
+// Rotary position embedding over [batch][seqlen][heads][head_dim] (element
+// strides xs / ys for batch, token, head; head_dim contiguous).
+struct RopeArgs {
+  const void *x;
+  void *y;
+  int64_t xs[3], ys[3];
+  int64_t seqlen, pos_offset;
+  double base;
+  int32_t batch, heads, head_dim, inverse;
+};
+
 // ---- launchers (return hipError_t of the launch) ----
 hipError_t launch_fwd_bf16(const FwdArgs &a, int hd, int64_t grid, hipStream_t s);
 hipError_t launch_fwd_f32(const FwdArgs &a, int hd, int64_t grid, hipStream_t s);
@@ -153,6 +164,8 @@ hipError_t launch_bwd_dq_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs &a, int hd, int64_t grid, int which, hipStream_t s);
 hipError_t launch_bwd_dq_f32(const BwdArgs &a, int hd, int64_t grid, hipStream_t s);
 hipError_t launch_bwd_dkdv_f32(const BwdArgs &a, int hd, int64_t grid, hipStream_t s);
+// head_dim even, 2..512
+hipError_t launch_rope(const RopeArgs &a, int dtype_bf16, hipStream_t s);
 
 // Fill rows of a [B][N][H][hd] tensor (strides) with zero; if lse != nullptr
 // also set lse [B][H][N] to -inf.

@@ -174,3 +174,30 @@ def test_calls_reject_bad_arguments_before_launch(bd):
     assert L.dfa_lse_merge(10, 96, fake, fake, fake, fake, nul) == bd.DFA_E_UNSUPPORTED
     assert L.dfa_lse_merge(10, 128, fake, nul, fake, fake, nul) == bd.DFA_E_NULL
     assert L.dfa_lse_merge(0, 128, nul, nul, nul, nul, nul) == 0
+
+
+def test_rope_argument_validation(bd):
+    """dfa_rope rejects bad arguments on the host, before any launch (no GPU
+    needed): the fake device addresses below are never dereferenced."""
+    L = bd.lib()
+    s = (ctypes.c_int64 * 3)(64 * 4 * 128, 4 * 128, 128)
+    s2 = (ctypes.c_int64 * 3)(64 * 4 * 128, 4 * 128, 130)
+    odd = (ctypes.c_int64 * 3)(64 * 4 * 128, 4 * 128, 127)
+    X, Y = ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000)
+
+    def call(dtype=bd.DFA_BF16, B=1, N=64, H=4, d=128, xs=s, x=X, ys=s, y=Y, off=0, base=1e4, inv=0):
+        return L.dfa_rope(dtype, B, N, H, d, xs, x, ys, y, off, base, inv, None)
+    assert call(N=0, x=None, y=None) == 0              # nothing to do
+    assert call(d=127) == bd.DFA_E_UNSUPPORTED
+    assert call(d=1024) == bd.DFA_E_UNSUPPORTED
+    assert call(dtype=7) == bd.DFA_E_UNSUPPORTED
+    assert call(x=None) == bd.DFA_E_NULL
+    assert call(xs=None) == bd.DFA_E_NULL
+    assert call(x=ctypes.c_void_p(0x10002)) == bd.DFA_E_ALIGN
+    assert call(dtype=bd.DFA_F32, y=ctypes.c_void_p(0x20004)) == bd.DFA_E_ALIGN
+    assert call(xs=odd) == bd.DFA_E_ALIGN
+    assert call(y=X, ys=s2) == bd.DFA_E_SHAPE             # in place needs equal strides
+    assert call(off=-1) == bd.DFA_E_SHAPE
+    assert call(base=0.0) == bd.DFA_E_SHAPE
+    assert call(base=float("nan")) == bd.DFA_E_SHAPE
+    assert call(inv=2) == bd.DFA_E_SHAPE
