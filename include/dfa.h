@@ -198,8 +198,9 @@ dfa_status dfa_schedule_build(int32_t kind, int64_t seqlen, int32_t n_ranks, dfa
  * of rank (r - s) mod P, as in DFA_SCHED_STRIPED.  Blocks have run = stripe and
  * stride = P * stride; stripe = 1 reproduces DFA_SCHED_STRIPED exactly.
  *   seqlen : N with N % (n_ranks * stripe) == 0, else DFA_E_SHAPE.
- *   stripe : >= 1.  The attention calls take run = 1 or run % 64 == 0 (their
- *            row tiles are 64 rows); other stripes are only enumerated.
+ *   stripe : >= 1.  The attention calls take run = 1 or run = 64 * 2^k (their
+ *            row tiles are 64 rows, and a tile's run is found by a shift);
+ *            other stripes are only enumerated.
  * Other arguments as dfa_schedule_build.
  */
 dfa_status dfa_schedule_build_striped_blocks(int64_t seqlen, int32_t n_ranks, int64_t stripe,

@@ -76,7 +76,7 @@ dfa_status check_block(const dfa_attn_desc *d, const dfa_block &b) {
     // whole runs that never overlap; the row tiles (64 rows) must not
     // straddle a run
     if (b.stride < b.run || b.len_q % b.run || b.len_kv % b.run) return DFA_E_SHAPE;
-    if (b.run % 64) return DFA_E_UNSUPPORTED;
+    if (b.run % 64 || ((b.run / 64) & (b.run / 64 - 1))) return DFA_E_UNSUPPORTED;  // 64 * 2^k
   }
   const int64_t rq = (b.len_q - 1) / b.run, rk = (b.len_kv - 1) / b.run;  // last run index
   if (b.q_start > N - 1 || rq > (N - 1 - b.q_start) / b.stride ||

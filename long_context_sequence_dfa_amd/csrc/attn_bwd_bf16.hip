@@ -69,6 +69,15 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
     return RUNS ? piece_pos(start, seg.stride, seg.run, i) : start + i * seg.stride;
   };
   const int64_t rs = RUNS ? piece_row_step(seg.stride, seg.run) : seg.stride;  // row step in a tile
+  // global position of the first row of 64-row tile t of a piece (a run is
+  // 64 * 2^tsh rows, so the tile's run and offset are a shift and a mask)
+  const int tsh = RUNS && seg.run > 1 ? __builtin_ctzll(static_cast<uint64_t>(seg.run)) - 6 : 0;
+  auto tile_pos = [&](int64_t start, int64_t t_) {
+    if constexpr (RUNS) {
+      if (seg.run > 1) return start + (t_ >> tsh) * seg.stride + ((t_ & ((int64_t{1} << tsh) - 1)) << 6);
+    }
+    return start + t_ * (DQ_BK * seg.stride);
+  };
   const int64_t q_last = RUNS ? pos_of(seg.q_start, iend - 1) : 0;
   const int64_t gq_w = RUNS ? pos_of(seg.q_start, i0w) : 0;
   // packed documents: this lane's row sees keys at positions >= qlo only;
@@ -133,7 +142,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
   int issued = 0;
   auto issue = [&](int stage) {
     const int64_t jt = tl_ * DQ_BK;
-    const int64_t p0 = pos_of(lw.kv_start, jt);
+    const int64_t p0 = tile_pos(lw.kv_start, tl_);
     ld.load(kb + 2 * p0 * G.ks[1], vb + 2 * p0 * G.vs[1], lds0 + stage * STAGE,
             lds0 + stage * STAGE + TB, lw.len_kv - jt);
     ++issued;
@@ -180,7 +189,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
     // this wave's row ii sees the tile's key jj iff jj <= ii + dw
     int64_t dw;
     if constexpr (RUNS) {
-      const int64_t gk = pos_of(cw.kv_start, j0);
+      const int64_t gk = tile_pos(cw.kv_start, t);
       dw = rs == 1 ? gq_w - gk : floor_div64(gq_w - gk, rs);
     } else {
       dw = i0w + cw.diag - j0;
@@ -188,7 +197,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
     if (dw + 31 >= 0) {
       const char *kt = smem + (it % NS) * STAGE;
       const char *vt = kt + TB;
-      const int64_t gk = DOCS ? pos_of(cw.kv_start, j0) : 0;  // position of key 0 of the tile
+      const int64_t gk = DOCS ? tile_pos(cw.kv_start, t) : 0;  // position of key 0 of the tile
       const bool need_mask = (dw < DQ_BK - 1) || (j0 + DQ_BK > cw.len_kv) || (DOCS && gk < qlo_w);
       int x = 0;
       unsigned span = 0;
@@ -301,6 +310,15 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
   };
   const int64_t pos = pos_of(seg.kv_start, valid ? col : seg.len_kv - 1);
   const int64_t rs = RUNS ? piece_row_step(seg.stride, seg.run) : seg.stride;  // row step in a tile
+  // global position of the first row of 64-row tile t of a piece (a run is
+  // 64 * 2^tsh rows, so the tile's run and offset are a shift and a mask)
+  const int tsh = RUNS && seg.run > 1 ? __builtin_ctzll(static_cast<uint64_t>(seg.run)) - 6 : 0;
+  auto tile_pos = [&](int64_t start, int64_t t_) {
+    if constexpr (RUNS) {
+      if (seg.run > 1) return start + (t_ >> tsh) * seg.stride + ((t_ & ((int64_t{1} << tsh) - 1)) << 6);
+    }
+    return start + t_ * (KV_BQ * seg.stride);
+  };
   // global positions of the workgroup's and this wave's first key
   const int64_t gk0 = RUNS ? pos_of(seg.kv_start, j0) : 0;
   const int64_t gk_w = RUNS ? pos_of(seg.kv_start, j0w) : 0;
@@ -380,7 +398,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
   int issued = 0;
   auto issue = [&](int stage) {
     const int64_t i0 = tl_ * KV_BQ;
-    const int64_t p0 = pos_of(lw.q_start, i0);
+    const int64_t p0 = tile_pos(lw.q_start, tl_);
     const char *qb = static_cast<const char *>(a.q) + 2 * (b * G.qs[0] + p0 * G.qs[1] + lw.h * G.qs[2]);
     const char *db = static_cast<const char *>(a.dout) + 2 * (b * G.os[0] + p0 * G.os[1] + lw.h * G.os[2]);
     const unsigned sb = lds0 + stage * STAGE;
@@ -431,7 +449,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
     // query row qq of the tile sees this wave's key c32 iff c32 <= qq + dw
     int64_t dw;
     if constexpr (RUNS) {
-      const int64_t gq = pos_of(cw.q_start, qi0);
+      const int64_t gq = tile_pos(cw.q_start, t);
       dw = rs == 1 ? gq - gk_w : floor_div64(gq - gk_w, rs);
     } else {
       dw = qi0 + cw.diag - j0w;
@@ -444,9 +462,9 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
       const float *ddt = lt + KV_BQ;
       // local query qq (0..63) of the tile is kept iff lo <= qq < hi
       // packed documents: global position of the tile's first and last query
-      const int64_t gq0 = DOCS ? pos_of(cw.q_start, qi0) : 0;
-      const int64_t gql = DOCS ? pos_of(cw.q_start, (qi0 + KV_BQ < cw.len_q ? qi0 + KV_BQ : cw.len_q) - 1)
-                                   : 0;
+      const int64_t gq0 = DOCS ? tile_pos(cw.q_start, t) : 0;
+      // the tile's last row (tiles never straddle a run)
+      const int64_t gql = DOCS ? gq0 + ((qi0 + KV_BQ < cw.len_q ? KV_BQ : cw.len_q - qi0) - 1) * rs : 0;
       const bool need_mask = (dw < 31) || (qi0 + KV_BQ > cw.len_q) || (DOCS && gql >= khi_w);
       int lo = 0, hi = KV_BQ;
       if (need_mask) {

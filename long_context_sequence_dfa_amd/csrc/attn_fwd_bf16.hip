@@ -123,6 +123,15 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     return RUNS ? piece_pos(start, seg.stride, seg.run, i) : start + i * seg.stride;
   };
   const int64_t rs = RUNS ? piece_row_step(seg.stride, seg.run) : seg.stride;  // row step in a tile
+  // global position of the first row of 64-row tile t of a piece (a run is
+  // 64 * 2^tsh rows, so the tile's run and offset are a shift and a mask)
+  const int tsh = RUNS && seg.run > 1 ? __builtin_ctzll(static_cast<uint64_t>(seg.run)) - 6 : 0;
+  auto tile_pos = [&](int64_t start, int64_t t_) {
+    if constexpr (RUNS) {
+      if (seg.run > 1) return start + (t_ >> tsh) * seg.stride + ((t_ & ((int64_t{1} << tsh) - 1)) << 6);
+    }
+    return start + t_ * (BK * seg.stride);
+  };
   const int64_t q_last = RUNS ? pos_of(seg.q_start, iend - 1) : 0;
   // global position of this wave's first row (extrapolated past a ragged end:
   // only the mask's row comparisons use it)
@@ -193,7 +202,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   int issued = 0;
   auto issue = [&](int stage) {
     const int64_t j0 = tl * BK;
-    const int64_t p0 = pos_of(lw.kv_start, j0);
+    const int64_t p0 = tile_pos(lw.kv_start, tl);
     ld.load(kb + 2 * p0 * G.ks[1], vb + 2 * p0 * G.vs[1], lds0 + stage * STAGE,
             lds0 + stage * STAGE + TB, lw.len_kv - j0);
     ++issued;
@@ -222,7 +231,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     // positions, in units of the row step)
     int64_t dw;
     if constexpr (RUNS) {
-      const int64_t gk = pos_of(cw.kv_start, j0);
+      const int64_t gk = tile_pos(cw.kv_start, t);
       dw = rs == 1 ? gq_w - gk : floor_div64(gq_w - gk, rs);
     } else {
       dw = i0w + cw.diag - j0;
@@ -243,7 +252,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
       __builtin_amdgcn_s_setprio(0);
       // element i of s0 / s1 is key j0 + 32*(i/16) + 16*((i%16)/8) + 8g + i%8
       // (global position of key jj of the tile: gk + jj * rs)
-      const int64_t gk = DOCS ? pos_of(cw.kv_start, j0) : 0;
+      const int64_t gk = DOCS ? tile_pos(cw.kv_start, t) : 0;
       if ((dw < BK - 1) || (j0 + BK > cw.len_kv) || (DOCS && gk < qlo_w)) {
         // key j0 + jj is visible iff lo <= jj <= lim: lim from the causal
         // rule and the piece's end, lo from the row's document start

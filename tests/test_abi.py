@@ -165,6 +165,15 @@ def test_calls_reject_bad_arguments_before_launch(bd):
             bad[0, 8] = (bad[0, 3] - bad[0, 4]) // val  # keep diag_offset consistent
         assert L.dfa_attn_fwd(ctypes.byref(d), bad.ctypes.data_as(ctypes.c_void_p), len(bad), 0, fake,
                               fake, fake, fake, fake, nul, 0, nul) == want, field
+    # runs of 64 * 2^k tokens only (a tile's run is found by a shift): 192 is refused
+    d768 = desc(bd)
+    d768.seqlen = 768
+    for name in ("q_strides", "k_strides", "v_strides", "o_strides"):
+        h = 4 if name in ("q_strides", "o_strides") else 2
+        getattr(d768, name)[:] = [768 * h * 128, h * 128, 128]
+    s192 = np.ascontiguousarray(bd.dfa_schedule_build_striped_blocks(768, 2, 192))
+    assert L.dfa_attn_fwd(ctypes.byref(d768), s192.ctypes.data_as(ctypes.c_void_p), len(s192), 0, fake,
+                          fake, fake, fake, fake, nul, 0, nul) == bd.DFA_E_UNSUPPORTED
     blk = bd.DfaBlock(*[int(x) for x in blocks[0]])
     assert L.dfa_attn_block_fwd(ctypes.byref(desc(bd, head_dim=32)), ctypes.byref(blk), fake, fake,
                                 fake, fake, fake, nul) == bd.DFA_E_UNSUPPORTED
