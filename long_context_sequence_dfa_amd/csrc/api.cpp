@@ -29,7 +29,6 @@ namespace {
 
 using dfa::KvRef;
 using dfa::KvSeg;
-using dfa::MergeItem;
 using dfa::QRef;
 using dfa::QSeg;
 using dfa::Tile;
@@ -300,29 +299,26 @@ dfa_status check_blocks(const dfa_attn_desc *d, const dfa_block *blocks, int64_t
 }
 
 // Stepwise forward: rounds of blocks whose query pieces are distinct, in
-// ring-step order.
+// ring-step order.  Each round's launch merges every block's partial into
+// the accumulator rows of its queries (distinct rows: no two blocks of a
+// round write the same row).
 struct StepPlan {
-  std::vector<QSeg> segs;      // one per block, with its partial-buffer offset
-  std::vector<KvRef> kv;       // one per block
-  std::vector<Tile> tiles;     // per round, contiguous
-  std::vector<MergeItem> items;
+  std::vector<QSeg> segs;   // one per block
+  std::vector<KvRef> kv;    // one per block
+  std::vector<Tile> tiles;  // per round, contiguous
   struct Round {
-    int32_t tile_begin, tile_count, item_begin, item_count;
-    int64_t part_rows, max_len;
+    int32_t tile_begin, tile_count;
   };
   std::vector<Round> rounds;
-  int64_t max_part_rows = 0;
 };
 
-void plan_steps(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n, int tileq,
-                StepPlan &sp) {
+void plan_steps(const dfa_block *blocks, int64_t n, int tileq, StepPlan &sp) {
   std::vector<int64_t> idx(static_cast<size_t>(n));
   for (int64_t i = 0; i < n; ++i) idx[i] = i;
   std::stable_sort(idx.begin(), idx.end(), [&](int64_t a, int64_t b) {
     return std::make_tuple(blocks[a].step, blocks[a].rank, blocks[a].kv_start) <
            std::make_tuple(blocks[b].step, blocks[b].rank, blocks[b].kv_start);
   });
-  const int64_t BH = static_cast<int64_t>(d->batch) * d->heads_q;
   size_t pos = 0;
   while (pos < idx.size()) {
     const int64_t step = blocks[idx[pos]].step;
@@ -345,8 +341,7 @@ void plan_steps(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n, int 
       used[r].push_back(key);
     }
     for (const auto &rb : rounds) {
-      StepPlan::Round R{static_cast<int32_t>(sp.tiles.size()), 0,
-                        static_cast<int32_t>(sp.items.size()), 0, 0, 0};
+      StepPlan::Round R{static_cast<int32_t>(sp.tiles.size()), 0};
       for (int64_t bi : rb) {
         const dfa_block &b = blocks[bi];
         QSeg s{};
@@ -354,7 +349,6 @@ void plan_steps(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n, int 
         s.len_q = b.len_q;
         s.stride = b.stride;
         s.run = b.run;
-        s.part_off = R.part_rows;
         s.blk_begin = static_cast<int32_t>(sp.kv.size());
         s.blk_count = 1;
         sp.kv.push_back(KvRef{b.kv_start, b.len_kv, b.diag_offset});
@@ -362,13 +356,8 @@ void plan_steps(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n, int 
         sp.segs.push_back(s);
         const int64_t nt = ceil_div(b.len_q, tileq);
         for (int64_t t = 0; t < nt; ++t) sp.tiles.push_back(Tile{sid, static_cast<int32_t>(t)});
-        sp.items.push_back(MergeItem{b.q_start, b.len_q, b.stride, b.run, R.part_rows});
-        R.part_rows += BH * b.len_q;
-        R.max_len = std::max<int64_t>(R.max_len, b.len_q);
       }
       R.tile_count = static_cast<int32_t>(sp.tiles.size()) - R.tile_begin;
-      R.item_count = static_cast<int32_t>(sp.items.size()) - R.item_begin;
-      sp.max_part_rows = std::max<int64_t>(sp.max_part_rows, R.part_rows);
       sp.rounds.push_back(R);
     }
     pos = end;
@@ -380,7 +369,7 @@ struct FusedLayout {
   size_t segs, kv, tiles, total;
 };
 struct StepLayout {
-  size_t segs, kv, tiles, items, acc_o, acc_lse, part_o, part_lse, total;
+  size_t segs, kv, tiles, acc_o, acc_lse, total;
 };
 struct BwdLayout {
   size_t qsegs, qkv, qtiles, kvsegs, kvq, kvtiles, dd, lse2, total;
@@ -407,12 +396,9 @@ StepLayout step_layout(const dfa_attn_desc *d, const StepPlan &p) {
   L.segs = 0;
   L.kv = L.segs + vbytes(p.segs);
   L.tiles = L.kv + vbytes(p.kv);
-  L.items = L.tiles + vbytes(p.tiles);
-  L.acc_o = L.items + vbytes(p.items);
+  L.acc_o = L.tiles + vbytes(p.tiles);
   L.acc_lse = L.acc_o + align_up(rows * hd * sizeof(float));
-  L.part_o = L.acc_lse + align_up(rows * sizeof(float));
-  L.part_lse = L.part_o + align_up(static_cast<size_t>(p.max_part_rows) * hd * sizeof(float));
-  L.total = L.part_lse + align_up(static_cast<size_t>(p.max_part_rows) * sizeof(float));
+  L.total = L.acc_lse + align_up(rows * sizeof(float));
   return L;
 }
 
@@ -519,7 +505,7 @@ extern "C" dfa_status dfa_workspace_size(const dfa_attn_desc *d, const dfa_block
     st = plan_q(d, blocks, n_blocks, fwd_tile(d), p);
     if (st != DFA_OK) return st;
     StepPlan sp;
-    plan_steps(d, blocks, n_blocks, fwd_tile(d), sp);
+    plan_steps(blocks, n_blocks, fwd_tile(d), sp);
     *bytes = step_layout(d, sp).total;
   } else if (op == DFA_OP_BWD) {
     QPlan qp;
@@ -632,7 +618,7 @@ extern "C" dfa_status dfa_attn_fwd(const dfa_attn_desc *d, const dfa_block *bloc
 
   // stepwise
   StepPlan sp;
-  plan_steps(d, blocks, n_blocks, fwd_tile(d), sp);
+  plan_steps(blocks, n_blocks, fwd_tile(d), sp);
   const StepLayout L = step_layout(d, sp);
   st = check_ws(workspace, ws_bytes, L.total);
   if (st != DFA_OK) return st;
@@ -641,30 +627,23 @@ extern "C" dfa_status dfa_attn_fwd(const dfa_attn_desc *d, const dfa_block *bloc
   put(host, L.segs, sp.segs);
   put(host, L.kv, sp.kv);
   put(host, L.tiles, sp.tiles);
-  put(host, L.items, sp.items);
   st = upload(workspace, host, L.acc_o, s);
   if (st != DFA_OK) return st;
   float *acc_o = reinterpret_cast<float *>(ws + L.acc_o);
   float *acc_lse = reinterpret_cast<float *>(ws + L.acc_lse);
-  float *part_o = reinterpret_cast<float *>(ws + L.part_o);
-  float *part_lse = reinterpret_cast<float *>(ws + L.part_lse);
   const int64_t rows = BH * d->seqlen;
   st = hip_status(dfa::launch_acc_init(acc_o, acc_lse, rows, hd, s));
   if (st != DFA_OK) return st;
-  a.o = part_o;
-  a.lse = part_lse;
-  a.out_mode = 1;
+  // per round: every block's partial, merged into its query rows (mode 2)
+  a.o = acc_o;
+  a.lse = acc_lse;
+  a.out_mode = 2;
   a.segs = reinterpret_cast<const QSeg *>(ws + L.segs);
   a.kv = reinterpret_cast<const KvRef *>(ws + L.kv);
-  const MergeItem *items = reinterpret_cast<const MergeItem *>(ws + L.items);
   for (const auto &R : sp.rounds) {
     a.tiles = reinterpret_cast<const Tile *>(ws + L.tiles) + R.tile_begin;
     a.n_tiles = R.tile_count;
     st = hip_status(launch(a, static_cast<int64_t>(R.tile_count) * BH));
-    if (st != DFA_OK) return st;
-    st = hip_status(dfa::launch_merge_items(acc_o, acc_lse, part_o, part_lse, items + R.item_begin,
-                                            R.item_count, R.max_len, d->batch, d->heads_q,
-                                            d->seqlen, hd, s));
     if (st != DFA_OK) return st;
   }
   return hip_status(dfa::launch_finalize(acc_o, acc_lse, o, d->o_strides, d->dtype, lse,

@@ -351,6 +351,27 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
           *reinterpret_cast<bf16x4 *>(ob + 2 * d0) = v;
         }
       if (g == 0) a.lse[(static_cast<int64_t>(b) * G.hq + h) * G.seqlen + pos] = lse;
+    } else if (OUT == 2) {
+      // merge this block's normalised partial into the accumulator row of the
+      // same query (one ring step's blocks have distinct query rows)
+      const int64_t arow = (static_cast<int64_t>(b) * G.hq + h) * G.seqlen + pos_of(seg.q_start, row);
+      float *ao = static_cast<float *>(a.o) + arow * HD;
+      float wa, wp, lnew;
+      merge_weights(a.lse[arow], lse, wa, wp, lnew);
+      wp *= inv;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4 *p4 = reinterpret_cast<f32x4 *>(ao + 32 * dt + 8 * q4 + 4 * g);
+          const f32x4 av = *p4;
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[e] = (wa == 0.f ? 0.f : wa * av[e]) + (wp == 0.f ? 0.f : wp * acc[dt][4 * q4 + e]);
+          *p4 = v;
+        }
+      if (g == 0) a.lse[arow] = lnew;
     } else {
       const int64_t prow = seg.part_off + (static_cast<int64_t>(b) * G.hq + h) * seg.len_q + row;
       float *op = static_cast<float *>(a.o) + prow * HD;
@@ -375,6 +396,8 @@ void launch_fwd_docs(const FwdArgs &a, dim3 gr, hipStream_t s) {
   const dim3 bl(NT);
   if (a.out_mode == 0)
     hipLaunchKernelGGL((fwd_bf16_kernel<HD, 0, true, RUNS, DOCS>), gr, bl, 0, s, a);
+  else if (a.out_mode == 2)
+    hipLaunchKernelGGL((fwd_bf16_kernel<HD, 2, true, RUNS, DOCS>), gr, bl, 0, s, a);
   else if (a.segs)
     hipLaunchKernelGGL((fwd_bf16_kernel<HD, 1, true, RUNS, DOCS>), gr, bl, 0, s, a);
   else
@@ -392,7 +415,7 @@ void launch_fwd_variant(const FwdArgs &a, dim3 gr, hipStream_t s) {
 hipError_t launch_fwd_bf16(const FwdArgs &a, int hd, int64_t grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (a.out_mode == 0 && !a.segs) return hipErrorInvalidValue;
+  if (a.out_mode != 1 && !a.segs) return hipErrorInvalidValue;
   const dim3 gr(static_cast<unsigned>(grid));
   if (hd == 128) {
     if (a.runs)

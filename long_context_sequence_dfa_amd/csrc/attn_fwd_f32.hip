@@ -128,6 +128,17 @@ __global__ __launch_bounds__(TQ) void fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
     for (int c = 0; c < HD; ++c) op[c] = acc[c] * inv;
     a.lse[(static_cast<int64_t>(b) * G.hq + h) * G.seqlen + pos] = lse;
+  } else if (OUT == 2) {
+    // merge into the accumulator row (one ring step's rows are distinct)
+    const int64_t arow = (static_cast<int64_t>(b) * G.hq + h) * G.seqlen +
+                         piece_pos(seg.q_start, seg.stride, seg.run, row);
+    float *ao = static_cast<float *>(a.o) + arow * HD;
+    float wa, wp, lnew;
+    merge_weights(a.lse[arow], lse, wa, wp, lnew);
+    wp *= inv;
+#pragma unroll
+    for (int c = 0; c < HD; ++c) ao[c] = (wa == 0.f ? 0.f : wa * ao[c]) + (wp == 0.f ? 0.f : wp * acc[c]);
+    a.lse[arow] = lnew;
   } else {
     const int64_t prow = seg.part_off + (static_cast<int64_t>(b) * G.hq + h) * seg.len_q + row;
     float *op = static_cast<float *>(a.o) + prow * HD;
@@ -146,11 +157,15 @@ hipError_t launch_fwd_f32(const FwdArgs &a, int hd, int64_t grid, hipStream_t s)
   if (hd == 128) {
     if (a.out_mode == 0)
       hipLaunchKernelGGL((fwd_f32_kernel<128, 0>), gr, bl, 0, s, a);
+    else if (a.out_mode == 2)
+      hipLaunchKernelGGL((fwd_f32_kernel<128, 2>), gr, bl, 0, s, a);
     else
       hipLaunchKernelGGL((fwd_f32_kernel<128, 1>), gr, bl, 0, s, a);
   } else if (hd == 64) {
     if (a.out_mode == 0)
       hipLaunchKernelGGL((fwd_f32_kernel<64, 0>), gr, bl, 0, s, a);
+    else if (a.out_mode == 2)
+      hipLaunchKernelGGL((fwd_f32_kernel<64, 2>), gr, bl, 0, s, a);
     else
       hipLaunchKernelGGL((fwd_f32_kernel<64, 1>), gr, bl, 0, s, a);
   } else {

@@ -137,6 +137,25 @@ __device__ __forceinline__ void sched_lds_ahead() {
   __builtin_amdgcn_sched_group_barrier(0x008, D, 0);
 }
 
+// Weights of the log-sum-exp merge of two normalised partials of one row
+// (Striped Attention Guide, "Algorithmic Mechanics" 1, steps 4-6, with each
+// partial already divided by its own row sum): LSE = M + ln(e^{la-M} + e^{lp-M}),
+// O = wa O_acc + wp O_part.  Two empty rows (-inf) give weights 0 and -inf.
+__device__ __forceinline__ void merge_weights(float la, float lp, float &wa, float &wp,
+                                              float &lse) {
+  const float M = fmaxf(la, lp);
+  if (M == -INFINITY) {
+    wa = 0.f;
+    wp = 0.f;
+    lse = -INFINITY;
+    return;
+  }
+  const float ea = expf(la - M), ep = expf(lp - M);
+  lse = M + logf(ea + ep);
+  wa = expf(la - lse);
+  wp = expf(lp - lse);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) {
   return __uint_as_float(static_cast<uint32_t>(u) << 16);
 }

@@ -40,7 +40,7 @@ __host__ __device__ inline int64_t floor_div64(int64_t a, int64_t b) {
 // pieces share the query piece's stride and run.
 struct QSeg {
   int64_t q_start, len_q, stride, run;
-  int64_t part_off;  // stepwise/block mode: float offset of this piece's partial buffer
+  int64_t part_off;  // single-block mode: float offset of this piece's partial buffer
   int32_t blk_begin, blk_count;
 };
 
@@ -97,13 +97,16 @@ __device__ inline void doc_range(const int32_t *b, int n, int64_t p, int64_t &lo
 struct FwdArgs {
   Geom g;
   const void *q, *k, *v;
-  void *o;        // out_mode 0: dtype O (strides g.os); 1: fp32 partial buffer base
-  float *lse;     // out_mode 0: [B][Hq][N]; 1: partial LSE base (float offset part_off/hd)
+  void *o;        // out_mode 0: dtype O (strides g.os); 1: fp32 partial buffer base;
+                  // 2: fp32 accumulator [B][Hq][N][hd]
+  float *lse;     // out_mode 0 and 2: [B][Hq][N]; 1: partial LSE base (float offset part_off/hd)
   const QSeg *segs;
   const KvRef *kv;
   const Tile *tiles;
   int32_t n_tiles;
-  int32_t out_mode;  // 0: final O/LSE at global rows; 1: fp32 partials per piece
+  int32_t out_mode;  // 0: final O/LSE at global rows; 1: fp32 partials per piece;
+                     // 2: partials merged into the accumulator rows (rows of one
+                     // launch are distinct)
   int32_t runs;      // some piece is made of runs (run > 1)
   QSeg seg0;         // used when segs == nullptr (one block, no table)
   KvRef kv0;
@@ -128,10 +131,6 @@ struct BwdArgs {
   int32_t runs;  // some piece is made of runs (run > 1)
 };
 
-// Row map of one partial buffer onto accumulator rows (stepwise merge).
-struct MergeItem {
-  int64_t q_start, len_q, stride, run, part_off;
-};
 
 // Tile shapes (rows per work item).
 constexpr int kFwdWaves = 8;                // bf16 forward: waves per workgroup
@@ -173,13 +172,6 @@ hipError_t launch_zero_rows(void *x, const int64_t strides[3], int dtype, int ba
                             int heads, int hd, float *lse, hipStream_t s);
 // acc <- identity (O = 0, LSE = -inf) for [rows][hd] fp32 + [rows].
 hipError_t launch_acc_init(float *o_acc, float *lse_acc, int64_t rows, int hd, hipStream_t s);
-// Merge partial rows into accumulators.  Item k of `items` maps its partial
-// rows [b][h][i] (at part_off) onto accumulator rows [b][h][q_start + i*stride]
-// of an accumulator [B][Hq][N][hd].
-hipError_t launch_merge_items(float *o_acc, float *lse_acc, const float *o_part,
-                              const float *lse_part, const MergeItem *items, int n_items,
-                              int64_t max_rows, int batch, int hq, int64_t n, int hd,
-                              hipStream_t s);
 // Plain contiguous merge of n_rows rows (public dfa_lse_merge).
 hipError_t launch_merge_rows(float *o_acc, float *lse_acc, const float *o_part,
                              const float *lse_part, int64_t n_rows, int hd, hipStream_t s);

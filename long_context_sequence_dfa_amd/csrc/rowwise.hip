@@ -15,51 +15,7 @@ namespace {
 
 constexpr int NT = 256;
 
-__device__ __forceinline__ void merge_weights(float la, float lp, float &wa, float &wp,
-                                              float &lse) {
-  const float M = fmaxf(la, lp);
-  if (M == -INFINITY) {
-    wa = 0.f;
-    wp = 0.f;
-    lse = -INFINITY;
-    return;
-  }
-  const float ea = expf(la - M), ep = expf(lp - M);
-  lse = M + logf(ea + ep);
-  wa = expf(la - lse);
-  wp = expf(lp - lse);
-}
-
 // one thread per (row, 4 floats); HD/4 threads of a row sit in one wave
-template <int HD>
-__global__ __launch_bounds__(NT) void merge_items_kernel(float *o_acc, float *lse_acc,
-                                                         const float *o_part,
-                                                         const float *lse_part,
-                                                         const MergeItem *items, int batch,
-                                                         int hq, int64_t n) {
-  constexpr int C4 = HD / 4;
-  const MergeItem it = items[blockIdx.y];
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
-  const int64_t rows = static_cast<int64_t>(batch) * hq * it.len_q;
-  if (tid >= rows * C4) return;
-  const int64_t prow = tid / C4;
-  const int c = static_cast<int>(tid % C4);
-  const int64_t bh = prow / it.len_q, i = prow % it.len_q;
-  const int64_t arow = bh * n + piece_pos(it.q_start, it.stride, it.run, i);
-  const float lp = lse_part[it.part_off + prow];
-  const float la = lse_acc[arow];
-  float wa, wp, lse;
-  merge_weights(la, lp, wa, wp, lse);
-  f32x4 *oa = reinterpret_cast<f32x4 *>(o_acc + arow * HD) + c;
-  const f32x4 op = reinterpret_cast<const f32x4 *>(o_part + (it.part_off + prow) * HD)[c];
-  const f32x4 av = *oa;
-  f32x4 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) r[e] = (wa == 0.f ? 0.f : wa * av[e]) + (wp == 0.f ? 0.f : wp * op[e]);
-  *oa = r;
-  if (c == 0) lse_acc[arow] = lse;
-}
-
 template <int HD>
 __global__ __launch_bounds__(NT) void merge_rows_kernel(float *o_acc, float *lse_acc,
                                                         const float *o_part,
@@ -178,22 +134,6 @@ hipError_t launch_acc_init(float *o_acc, float *lse_acc, int64_t rows, int hd, h
   const int64_t th = rows * (hd / 4) > rows ? rows * (hd / 4) : rows;
   if (th == 0) return hipSuccess;
   hipLaunchKernelGGL(acc_init_kernel, dim3(blocks_for(th)), dim3(NT), 0, s, o_acc, lse_acc, rows, hd);
-  return hipGetLastError();
-}
-
-hipError_t launch_merge_items(float *o_acc, float *lse_acc, const float *o_part,
-                              const float *lse_part, const MergeItem *items, int n_items,
-                              int64_t max_rows, int batch, int hq, int64_t n, int hd,
-                              hipStream_t s) {
-  if (n_items == 0 || max_rows == 0) return hipSuccess;
-  const int64_t th = static_cast<int64_t>(batch) * hq * max_rows * (hd / 4);
-  dim3 gr(blocks_for(th), n_items);
-  if (hd == 128)
-    hipLaunchKernelGGL(merge_items_kernel<128>, gr, dim3(NT), 0, s, o_acc, lse_acc, o_part,
-                       lse_part, items, batch, hq, n);
-  else
-    hipLaunchKernelGGL(merge_items_kernel<64>, gr, dim3(NT), 0, s, o_acc, lse_acc, o_part,
-                       lse_part, items, batch, hq, n);
   return hipGetLastError();
 }
 
