@@ -7,15 +7,17 @@
 //   P_ij = e^{scale q_i.k_j - LSE_i},  dP_ij = dO_i.v_j,  dS_ij = P_ij (dP_ij - D_i)
 //   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i.
 //
-// Two kernels, no atomics, deterministic:
-//  * dq: query-major, shaped like the forward -- a workgroup owns 128 query
+// Three kernels, no atomics, deterministic (8 waves, 32 rows per wave):
+//  * dq: query-major, shaped like the forward -- a workgroup owns 256 query
 //    rows, walks its query piece's blocks in ring-step order and computes
 //    S^T = K Q^T, dP^T = V dO^T and dQ^T += K^T dS^T on the matrix cores.
 //    Each lane owns one query column, so LSE_i and D_i are per-lane scalars.
-//  * dkdv: key-major -- a workgroup owns 128 key rows (K and V live in
-//    registers as MFMA operands), walks every block that reads its key piece
-//    and every query head of its group, and computes S = Q K^T, dP = dO V^T,
-//    dV^T += dO^T P and dK^T += Q^T dS.  Each lane owns one key column.
+//  * dkdv (two variants, dK and dV): key-major -- a workgroup owns 256 key
+//    rows (K, and for dK also V, live in registers as MFMA operands), walks
+//    every block that reads its key piece and every query head of its group,
+//    and computes S = Q K^T, then dV^T += dO^T P, or dP = dO V^T and
+//    dK^T += Q^T dS.  Each lane owns one key column.  One accumulator set
+//    per wave keeps two waves on every SIMD.
 // With packed documents (Striped Attention Guide, "Production Deployment and
 // Best Practices", item 3) a pair is kept only inside one document: the
 // query-major kernel masks keys before the row's document start, the
