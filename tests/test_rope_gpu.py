@@ -73,9 +73,14 @@ def test_rope_in_place_and_strided(dfa):
     out = torch.empty_like(tx)
     dfa.dfa_rope(tx, out)
     ref = dfa.dfa_rope(tx.contiguous())
+    # rows that are not 16-byte aligned (2-element offset, odd row stride): the one-pair path
+    pad = torch.zeros((B, N, H, d + 2), dtype=torch.bfloat16, device="cuda")
+    odd = pad[..., 2:]
+    odd.copy_(tx)
+    dfa.dfa_rope(odd, odd)
     dfa.dfa_rope(tx, tx)  # in place
     torch.cuda.synchronize()
-    assert torch.equal(out, ref) and torch.equal(tx, ref)
+    assert torch.equal(out, ref) and torch.equal(tx, ref) and torch.equal(odd, ref)
 
 
 def test_attention_over_rotated_inputs(dfa):
