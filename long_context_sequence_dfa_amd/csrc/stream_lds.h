@@ -22,10 +22,7 @@ struct Tile64 {
   static constexpr int ROWS = 64;
   static constexpr int RB = HD * 2 + 32;             // row pitch in bytes
   static constexpr int TB = ROWS * RB;               // tile bytes
-  static constexpr int LPR = HD * 2 / 16;            // data lanes per row in a direct load
-  static constexpr int LPRP = RB / 16;               // lanes per row including the pad
-  static constexpr int RPI = 64 / LPRP;              // rows per direct-load instruction
-  static constexpr int NI = (ROWS + RPI - 1) / RPI;  // instructions per tile
+  static constexpr int LPR = HD * 2 / 16;            // 16-byte data chunks per row
 
   // b128 operand read: row kperm(c32) of a 32-row block, chunk pair 2 ks + g
   // (add 32 ks bytes and 32 RB per block)
@@ -101,33 +98,41 @@ __device__ __forceinline__ void vm_wait(int n) {
 
 // Direct loads of two 64-row tiles (separate row strides, e.g. K and V) into
 // the Tile64 layout by NW waves.  One instruction writes 64 lanes x 16
-// contiguous bytes, so LPRP lanes cover one padded row (pad lanes re-write the
-// row's first chunk into the pad).  Wave w issues instructions w, w + NW, ...;
-// each lane's row and chunk are fixed, so its byte offsets are computed once
-// (32-bit: the host guarantees that 64 rows span less than 2^31 bytes).  Rows
-// past the piece re-read its last row; the caller's mask drops them.
+// contiguous bytes of LDS, so instruction i fills the tile's padded 16-byte
+// chunks 64 i .. 64 i + 63 in row-major order: every lane of every
+// instruction is used (ROWS * RB / 1024 instructions per tile, exact), rows
+// simply continue across instruction boundaries, and a lane that lands on a
+// pad chunk re-reads its row's first data chunk.  Wave w issues instructions
+// w, w + NW, ...; a lane's source offsets are fixed, so they are computed
+// once (32-bit: the host guarantees that 64 rows span less than 2^31 bytes).
+// Rows past the piece re-read its last row; the caller's mask drops them.
 template <int HD, int NW>
 struct TileStream {
   using T = Tile64<HD>;
-  static constexpr int MW = (T::NI + NW - 1) / NW;  // instructions per wave and tensor (max)
-  int wv, l_row, l_p;
+  static constexpr int CPR = T::RB / 16;            // 16-byte chunks per padded row
+  static constexpr int NI = T::ROWS * CPR / 64;     // instructions per tile
+  static_assert(T::ROWS * CPR % 64 == 0, "a tile is a whole number of instructions");
+  static constexpr int MW = (NI + NW - 1) / NW;     // instructions per wave and tensor (max)
+  int wv, lane;
   unsigned rsa, rsb;
   unsigned oa[MW], ob[MW];
 
-  __device__ int lrow(int m) const { return (wv + NW * m) * T::RPI + l_row; }
-  __device__ int lchunk(int r) const { return l_p < T::LPR ? (l_p ^ ((r >> 3) & 1)) : 0; }
-  __device__ bool lane_on(int m) const { return l_row < T::RPI && lrow(m) < T::ROWS; }
   // instructions this wave issues per tensor and tile (wave-uniform)
-  __device__ int count() const { return wv < T::NI ? (T::NI - wv + NW - 1) / NW : 0; }
+  __device__ int count() const { return wv < NI ? (NI - wv + NW - 1) / NW : 0; }
+  // tile row and source chunk of this lane in instruction i
+  __device__ int row_of(int i) const { return (64 * i + lane) / CPR; }
+  __device__ int chunk_of(int i) const {
+    const int c = (64 * i + lane) % CPR;
+    return c < T::LPR ? c ^ ((row_of(i) >> 3) & 1) : 0;
+  }
 
-  __device__ TileStream(int wave, int lane, int64_t rs_a, int64_t rs_b)
-      : wv(wave), l_row(lane / T::LPRP), l_p(lane % T::LPRP),
-        rsa(static_cast<unsigned>(rs_a)), rsb(static_cast<unsigned>(rs_b)) {
+  __device__ TileStream(int wave, int lane_, int64_t rs_a, int64_t rs_b)
+      : wv(wave), lane(lane_), rsa(static_cast<unsigned>(rs_a)), rsb(static_cast<unsigned>(rs_b)) {
 #pragma unroll
     for (int m = 0; m < MW; ++m) {
-      const int r = lrow(m);
-      oa[m] = r * rsa + 16 * lchunk(r);
-      ob[m] = r * rsb + 16 * lchunk(r);
+      const int i = wv + NW * m, r = row_of(i), c = chunk_of(i);
+      oa[m] = r * rsa + 16 * c;
+      ob[m] = r * rsb + 16 * c;
     }
   }
 
@@ -136,26 +141,24 @@ struct TileStream {
   __device__ void load(const char *ga, const char *gb, unsigned la, unsigned lb, int64_t rows) const {
     if (rows >= T::ROWS) {
 #pragma unroll
-      for (int m = 0; m < MW; ++m)
-        if (wv + NW * m < T::NI) {
-          const unsigned r0 = (wv + NW * m) * T::RPI * T::RB;
-          if (lane_on(m)) {
-            dma16(ga, oa[m], la + r0);
-            dma16(gb, ob[m], lb + r0);
-          }
+      for (int m = 0; m < MW; ++m) {
+        const int i = wv + NW * m;
+        if (i < NI) {
+          dma16(ga, oa[m], la + 1024 * i);
+          dma16(gb, ob[m], lb + 1024 * i);
         }
+      }
     } else {
       const int last = static_cast<int>(rows - 1);
 #pragma unroll
-      for (int m = 0; m < MW; ++m)
-        if (wv + NW * m < T::NI) {
-          const unsigned r0 = (wv + NW * m) * T::RPI * T::RB;
-          if (lane_on(m)) {
-            const int r = lrow(m), rr = r < last ? r : last;
-            dma16(ga, rr * rsa + 16 * lchunk(r), la + r0);
-            dma16(gb, rr * rsb + 16 * lchunk(r), lb + r0);
-          }
+      for (int m = 0; m < MW; ++m) {
+        const int i = wv + NW * m;
+        if (i < NI) {
+          const int r = row_of(i), rr = r < last ? r : last, c = chunk_of(i);
+          dma16(ga, rr * rsa + 16 * c, la + 1024 * i);
+          dma16(gb, rr * rsb + 16 * c, lb + 1024 * i);
         }
+      }
     }
   }
 };
