@@ -83,8 +83,10 @@ enum { DFA_F32 = 0, DFA_BF16 = 1 };
 enum {
   DFA_FWD_FUSED = 0,   /* one launch; each query tile walks its rank's blocks in ring-step
                           order with the running max/sum/output in registers */
-  DFA_FWD_STEPWISE = 1 /* ring-faithful: per step, every rank's blocks emit partial
-                          (O, LSE) pairs that are merged into per-rank accumulators */
+  DFA_FWD_STEPWISE = 1 /* ring-faithful: per step, every rank's blocks compute partial
+                          (O, LSE) pairs that are merged into fp32 accumulators (the merge
+                          runs in the partial kernel's epilogue; one launch per round of
+                          blocks with distinct query rows) */
 };
 
 /* Operations for dfa_workspace_size. */
