@@ -10,10 +10,9 @@ resident in HBM.
 Throughput counts causal-effective FLOPs over the exact visible pairs:
 4*d per pair forward (QK^T and PV) and 10*d per pair backward (the recompute
 of S plus dP, dV, dK, dQ).  Per kernel the algorithmic share is: forward
-4*d; dV kernel 4*d (the recompute of S, and dV); dK kernel 4*d (dP and dK);
-dQ kernel 2*d (dQ).  Recomputations beyond those five backward products (S
-again in the dK and dQ kernels, dP again in the dQ kernel) are extra work and
-not counted.  The dominant kernel's roofline figure uses that share and the
+4*d; dK/dV kernel 8*d (the recompute of S, dV, dP and dK); dQ kernel 2*d
+(dQ).  Recomputations beyond those five backward products (S and dP again
+in the dQ kernel) are extra work and not counted.  The dominant kernel's roofline figure uses that share and the
 kernel's own average duration, read from HIP events recorded on the stream
 right before and after it (dfa_attn_bwd_ex marks).
 
@@ -308,7 +307,7 @@ def main() -> int:
 
     per = {name: float(np.mean([ev.elapsed(m[a], m[b]) for m in ev_all]))
            for name, a, b in (("fwd", 0, 1), ("bwd", 1, 6), ("bwd_pre", 2, 3), ("dq", 3, 4),
-                              ("dk", 4, 5), ("dv", 5, 6), ("rope_in", 7, 0), ("rope_back", 6, 8))}
+                              ("dkdv", 5, 6), ("rope_in", 7, 0), ("rope_back", 6, 8))}
     ms_step = elapsed * 1e3 / args.steps
     total_flops = (fwd_flops + bwd_flops) * args.steps
     value = total_flops / elapsed / 1e12
@@ -317,8 +316,7 @@ def main() -> int:
     # the dominant kernel by time, with its algorithmic FLOP share
     kernels = {"attn_fwd_bf16_fused": (per["fwd"], fwd_flops),
                "attn_bwd_dq_bf16": (per["dq"], 2.0 * D * pairs),
-               "attn_bwd_dk_bf16": (per["dk"], 4.0 * D * pairs),
-               "attn_bwd_dv_bf16": (per["dv"], 4.0 * D * pairs)}
+               "attn_bwd_dkdv_bf16": (per["dkdv"], 8.0 * D * pairs)}
     dom = max(kernels, key=lambda n: kernels[n][0])
     dom_ms, dom_flops = kernels[dom]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
@@ -343,7 +341,7 @@ def main() -> int:
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "fwd_ms": fwd_avg,
         "bwd_ms": bwd_avg,
-        "kernel_ms": {k_: per[k_] for k_ in ("fwd", "bwd_pre", "dq", "dk", "dv")},
+        "kernel_ms": {k_: per[k_] for k_ in ("fwd", "bwd_pre", "dq", "dkdv")},
         **({"rope_ms": {"q_k_forward": per["rope_in"], "dq_dk_back": per["rope_back"]},
             # q and k forward, dq and dk back: each pass reads and writes its bf16 tensor once
             "rope_gbs": 8.0 * (tq.numel() + tk.numel()) / ((per["rope_in"] + per["rope_back"]) * 1e-3) / 1e9}

@@ -281,9 +281,10 @@ dfa_status dfa_attn_bwd(const dfa_attn_desc *d, const dfa_block *blocks, int64_t
  * hipEvent_t (passed as void*) created by the caller; the call records it on
  * its stream right before the named kernel is launched, or (end) right after
  * its last launch.  Recording changes no result and skips no work.  The
- * backward launches, in order: D = rowsum(dO*O), the dQ kernel, the dK
- * kernel, the dV kernel.  (fp32 computes dK and dV in one kernel: dk_begin
- * and dv_begin are then recorded back to back before it.)
+ * backward launches, in order: D = rowsum(dO*O), the dQ kernel, and one
+ * kernel that computes both dK and dV: dk_begin and dv_begin are recorded
+ * back to back before it, so the dK-to-dV interval is empty and dv_begin to
+ * end times the dK/dV kernel.
  */
 typedef struct dfa_kernel_marks {
   void *pre_begin;

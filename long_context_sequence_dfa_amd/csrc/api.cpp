@@ -752,16 +752,11 @@ extern "C" dfa_status dfa_attn_bwd_ex(const dfa_attn_desc *d, const dfa_block *b
   st = hip_status(bf ? dfa::launch_bwd_dq_bf16(a, hd, a.n_qtiles * BHq, s)
                      : dfa::launch_bwd_dq_f32(a, hd, a.n_qtiles * BHq, s));
   if (st != DFA_OK) return st;
+  // one kernel computes dK and dV: both marks precede it
   if (marks) mark(marks->dk_begin);
-  if (bf) {
-    st = hip_status(dfa::launch_bwd_dkdv_bf16(a, hd, a.n_kvtiles * BHkv, 2, s));
-    if (st != DFA_OK) return st;
-    if (marks) mark(marks->dv_begin);
-    st = hip_status(dfa::launch_bwd_dkdv_bf16(a, hd, a.n_kvtiles * BHkv, 1, s));
-  } else {
-    if (marks) mark(marks->dv_begin);
-    st = hip_status(dfa::launch_bwd_dkdv_f32(a, hd, a.n_kvtiles * BHkv, s));
-  }
+  if (marks) mark(marks->dv_begin);
+  st = hip_status(bf ? dfa::launch_bwd_dkdv_bf16(a, hd, a.n_kvtiles * BHkv, s)
+                     : dfa::launch_bwd_dkdv_f32(a, hd, a.n_kvtiles * BHkv, s));
   if (st != DFA_OK) return st;
   if (marks) mark(marks->end);
   return mark_ok ? DFA_OK : DFA_E_HIP;

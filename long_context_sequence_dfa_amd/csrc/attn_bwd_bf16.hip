@@ -7,25 +7,26 @@
 //   P_ij = e^{scale q_i.k_j - LSE_i},  dP_ij = dO_i.v_j,  dS_ij = P_ij (dP_ij - D_i)
 //   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i.
 //
-// Three kernels, no atomics, deterministic (8 waves, 32 rows per wave):
+// Two kernels, no atomics, deterministic (8 waves, 32 rows per wave):
 //  * dq: query-major, shaped like the forward -- a workgroup owns 256 query
 //    rows, walks its query piece's blocks in ring-step order and computes
 //    S^T = K Q^T, dP^T = V dO^T and dQ^T += K^T dS^T on the matrix cores.
 //    Each lane owns one query column, so LSE_i and D_i are per-lane scalars.
-//  * dkdv (two variants, dK and dV): key-major -- a workgroup owns 256 key
-//    rows (K, and for dK also V, live in registers as MFMA operands), walks
-//    every block that reads its key piece and every query head of its group,
-//    and computes S = Q K^T, then dV^T += dO^T P, or dP = dO V^T and
-//    dK^T += Q^T dS.  Each lane owns one key column.  One accumulator set
-//    per wave keeps two waves on every SIMD.
+//  * dkdv: key-major -- a workgroup owns 256 key rows, walks every block
+//    that reads its key piece and every query head of its group, and
+//    computes S = Q K^T, dV^T += dO^T P, dP = dO V^T and dK^T += Q^T dS, so
+//    S and P are formed once for both gradients.  Each lane owns one key
+//    column.  K lives in registers as an MFMA operand; the V operand is
+//    parked in LDS, which keeps the two accumulator sets of a wave within
+//    the 256 registers that let two waves share every SIMD.
 // With packed documents (Striped Attention Guide, "Production Deployment and
 // Best Practices", item 3) a pair is kept only inside one document: the
 // query-major kernel masks keys before the row's document start, the
 // key-major ones queries at or after the key's document end, and both skip
 // the tiles no row of the workgroup can see.
-// Both stream 64-row K/V (or Q/dO) tiles through NS LDS stages with direct
-// loads issued NS - 1 tiles ahead (stream_lds.h); transposed operands come
-// from ds_read_b64_tr_b16 on the row-major tiles.
+// Both stream 64-row K/V (or Q/dO) tiles through LDS stages with direct
+// loads issued one stage ahead of the oldest resident tile (stream_lds.h);
+// transposed operands come from ds_read_b64_tr_b16 on the row-major tiles.
 #include "dfa_internal.h"
 #include "stream_lds.h"
 
@@ -273,15 +274,16 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
 // ========================= dK, dV (key-major) =========================
 constexpr int KV_BK = kBwdTileKV;  // 32 key rows per wave
 constexpr int KV_BQ = 64;          // query rows per streamed tile
+constexpr int KV_NS = kKvStages;   // Q/dO tiles resident in LDS
 static_assert(KV_BK == 32 * NW, "one 32-key column block per wave");
 
-// Key-major gradient kernels.  MODE 1 accumulates dV^T += dO^T P (needs S
-// only), MODE 2 accumulates dK^T += Q^T dS (needs S and dP).  Splitting the
-// two keeps one 64-register accumulator set per wave, so two waves share each
-// SIMD and hide each other's LDS and exponent latency; S is recomputed in both.
-constexpr int KV_DV = 1, KV_DK = 2;
-
-template <int HD, int MODE, bool RUNS, bool DOCS>
+// Key-major gradient kernel: per (key tile, query tile) pair S, P, dV, dP,
+// dS and dK, in that order.  Registers per lane: K operand 4 HD/16, two
+// accumulator sets 2 HD/2, one 32-query slice of S and dP; the V operand
+// (HD/16 fragments of 16 bytes per lane) waits in LDS, where each lane reads
+// back only what it wrote.  LDS: KV_NS stages of Q, dO and the row
+// statistics plus the parked V fragments of the workgroup.
+template <int HD, bool RUNS, bool DOCS>
 __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
   using TL = Tile64<HD>;
   static_assert(TL::ROWS == KV_BQ, "query tiles are 64 rows");
@@ -289,8 +291,9 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
   constexpr int TB = TL::TB;
   constexpr int STAGE = 2 * TB + 2 * KV_BQ * 4;  // Q, dO, LSE*log2(e), D
   constexpr int KS = HD / 16, DT = HD / 32;
-  constexpr bool DK = MODE == KV_DK;
-  __shared__ __attribute__((aligned(16))) char smem[NS * STAGE];
+  constexpr int VPARK = KS * 1024;               // parked V fragments per wave
+  static_assert(KV_NS * STAGE + NW * VPARK <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(16))) char smem[KV_NS * STAGE + NW * VPARK];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -417,25 +420,32 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
     next(gl, kl, tl_, lw);
   };
 #pragma unroll
-  for (int st = 0; st < NS - 1; ++st)
+  for (int st = 0; st < KV_NS - 1; ++st)
     if (gl < ngrp) issue(st);
 
-  // K (and for dK also V) as B operands of S = Q K^T and dP = dO V^T; rows
-  // past the key piece read its last row and are never stored
-  bf16x8 kf[KS], vf[DK ? KS : 1];
+  // K and V as B operands of S = Q K^T and dP = dO V^T: lane (c32, g) holds
+  // row c32's elements 16 ks + 8 g .. +8.  Rows past the key piece read its
+  // last row and are never stored.  V's fragments go to this lane's own
+  // 16-byte slots of the parking area (slot ks at 1024 ks: a wave's reads of
+  // one slot cover 1 KB without bank conflicts).
+  bf16x8 kf[KS];
+  char *vpark = smem + KV_NS * STAGE + wave * VPARK + lane * 16;
   {
     const char *ksrc = static_cast<const char *>(a.k) + 2 * (b * G.ks[0] + pos * G.ks[1] + hk * G.ks[2]);
     const char *vsrc = static_cast<const char *>(a.v) + 2 * (b * G.vs[0] + pos * G.vs[1] + hk * G.vs[2]);
+    bf16x8 vf[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       kf[ks] = __builtin_bit_cast(bf16x8, ld16(ksrc + (2 * ks + g) * 16));
-      if (DK) vf[ks] = __builtin_bit_cast(bf16x8, ld16(vsrc + (2 * ks + g) * 16));
+      vf[ks] = __builtin_bit_cast(bf16x8, ld16(vsrc + (2 * ks + g) * 16));
     }
-  }
-  vm_wait<0>();
-  f32x16 acc[DT];
+    vm_wait<0>();
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
+    for (int ks = 0; ks < KS; ++ks) *reinterpret_cast<bf16x8 *>(vpark + ks * 1024) = vf[ks];
+  }
+  f32x16 acck[DT], accv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acck[dt] = accv[dt] = f32x16{};
 
   // per-lane operand offsets (independent of the tile); loop indices only
   // add compile-time constants to them
@@ -445,7 +455,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
   while (gi < ngrp) {
     vm_wait((issued - 1 - it) * per_tile);  // this wave's part of tile `it` landed
     __syncthreads();                        // every part landed; stage it-1 free
-    if (gl < ngrp) issue((it + NS - 1) % NS);
+    if (gl < ngrp) issue((it + KV_NS - 1) % KV_NS);
 
     const int64_t qi0 = t * KV_BQ;
     // query row qq of the tile sees this wave's key c32 iff c32 <= qq + dw
@@ -458,7 +468,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
     }
     // some pair of this wave visible: largest query row sees smallest key row
     if (KV_BQ - 1 + dw >= 0) {
-      const char *qt = smem + (it % NS) * STAGE;
+      const char *qt = smem + (it % KV_NS) * STAGE;
       const char *dt_ = qt + TB;
       const float *lt = reinterpret_cast<const float *>(qt + 2 * TB);
       const float *ddt = lt + KV_BQ;
@@ -482,14 +492,12 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {  // two halves of 32 query rows
-        f32x16 s = f32x16{}, dpm = f32x16{};
         const char *qa = qt + a_off + 32 * mt * RB, *da = dt_ + a_off + 32 * mt * RB;
+        f32x16 s = f32x16{};
         __builtin_amdgcn_s_setprio(1);  // see the dQ kernel
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          s = mfma32(__builtin_bit_cast(bf16x8, ld16(qa + ks * 32)), kf[ks], s);
-          if (DK) dpm = mfma32(__builtin_bit_cast(bf16x8, ld16(da + ks * 32)), vf[ks], dpm);
-        }
+        for (int ks = 0; ks < KS; ++ks) s = mfma32(__builtin_bit_cast(bf16x8, ld16(qa + ks * 32)), kf[ks], s);
+        sched_lds_ahead<KS, 2>();
         __builtin_amdgcn_s_setprio(0);
         // element i is query row qi0 + 32mt + 16(i/8) + 8g + i%8; masked
         // scores become -inf (probability 0)
@@ -502,33 +510,59 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
             if (rel >= span) s[i] = -INFINITY;
           }
         }
-        bf16x8 ob[2];
+        // P (fp32, in place of S: it is needed again for dS) and its bf16
+        // copy, the B operand of dV
+        bf16x8 pb[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int qoff = 32 * mt + 16 * u + 8 * g;
           const f32x4 la = *reinterpret_cast<const f32x4 *>(lt + qoff);
           const f32x4 lb = *reinterpret_cast<const f32x4 *>(lt + qoff + 4);
-          f32x4 da4 = f32x4{}, db4 = f32x4{};
-          if (DK) {
-            da4 = *reinterpret_cast<const f32x4 *>(ddt + qoff);
-            db4 = *reinterpret_cast<const f32x4 *>(ddt + qoff + 4);
-          }
 #pragma unroll
           for (int w = 0; w < 8; ++w) {
             const int i = 8 * u + w;
-            const float p = fast_exp2(__builtin_fmaf(s[i], c, -(w < 4 ? la[w] : lb[w - 4])));
-            ob[u][w] = static_cast<__bf16>(DK ? p * (dpm[i] - (w < 4 ? da4[w] : db4[w - 4])) : p);
+            s[i] = fast_exp2(__builtin_fmaf(s[i], c, -(w < 4 ? la[w] : lb[w - 4])));
+            pb[u][w] = static_cast<__bf16>(s[i]);
           }
         }
-        // dV^T += dO^T P or dK^T += Q^T dS: A operand read transposed from LDS
-        const char *src = DK ? qt : dt_;
+        // dV^T += dO^T P: A operand read transposed from the dO tile
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int o = t_off + 16 * (2 * mt + u) * RB;
 #pragma unroll
           for (int e = 0; e < DT; ++e)
-            acc[e] = mfma32(cat8(lds_read_tr(src + o + 64 * e), lds_read_tr(src + o + 4 * RB + 64 * e)),
-                            ob[u], acc[e]);
+            accv[e] = mfma32(cat8(lds_read_tr(dt_ + o + 64 * e), lds_read_tr(dt_ + o + 4 * RB + 64 * e)),
+                             pb[u], accv[e]);
+        }
+        // dP = dO V^T, then dS = P (dP - D)
+        f32x16 dpm = f32x16{};
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          dpm = mfma32(__builtin_bit_cast(bf16x8, ld16(da + ks * 32)),
+                       *reinterpret_cast<const bf16x8 *>(vpark + ks * 1024), dpm);
+        sched_lds_ahead<KS, 2>();
+        __builtin_amdgcn_s_setprio(0);
+        bf16x8 sb[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int qoff = 32 * mt + 16 * u + 8 * g;
+          const f32x4 da4 = *reinterpret_cast<const f32x4 *>(ddt + qoff);
+          const f32x4 db4 = *reinterpret_cast<const f32x4 *>(ddt + qoff + 4);
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            const int i = 8 * u + w;
+            sb[u][w] = static_cast<__bf16>(s[i] * (dpm[i] - (w < 4 ? da4[w] : db4[w - 4])));
+          }
+        }
+        // dK^T += Q^T dS: A operand read transposed from the Q tile
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int o = t_off + 16 * (2 * mt + u) * RB;
+#pragma unroll
+          for (int e = 0; e < DT; ++e)
+            acck[e] = mfma32(cat8(lds_read_tr(qt + o + 64 * e), lds_read_tr(qt + o + 4 * RB + 64 * e)),
+                             sb[u], acck[e]);
         }
       }
     }
@@ -536,17 +570,22 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
     ++it;
   }
   if (!valid) return;
-  char *out = DK ? static_cast<char *>(a.dk) + 2 * (b * G.ks[0] + pos * G.ks[1] + hk * G.ks[2])
-                 : static_cast<char *>(a.dv) + 2 * (b * G.vs[0] + pos * G.vs[1] + hk * G.vs[2]);
-  const float osc = DK ? G.scale : 1.f;
+  // dK = scale * acck, dV = accv; element 4 q4 + e of block dt is column
+  // 32 dt + 8 q4 + 4 g + e of this lane's key row
+  char *dko = static_cast<char *>(a.dk) + 2 * (b * G.ks[0] + pos * G.ks[1] + hk * G.ks[2]);
+  char *dvo = static_cast<char *>(a.dv) + 2 * (b * G.vs[0] + pos * G.vs[1] + hk * G.vs[2]);
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-      bf16x4 x;
+      bf16x4 xk, xv;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = static_cast<__bf16>(acc[dt][4 * q4 + e] * osc);
-      *reinterpret_cast<bf16x4 *>(out + 2 * (32 * dt + 8 * q4 + 4 * g)) = x;
+      for (int e = 0; e < 4; ++e) {
+        xk[e] = static_cast<__bf16>(acck[dt][4 * q4 + e] * G.scale);
+        xv[e] = static_cast<__bf16>(accv[dt][4 * q4 + e]);
+      }
+      *reinterpret_cast<bf16x4 *>(dko + 2 * (32 * dt + 8 * q4 + 4 * g)) = xk;
+      *reinterpret_cast<bf16x4 *>(dvo + 2 * (32 * dt + 8 * q4 + 4 * g)) = xv;
     }
 }
 
@@ -580,38 +619,28 @@ hipError_t launch_bwd_dq_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_
   return hipGetLastError();
 }
 
-template <int HD, int MODE, bool RUNS>
+template <int HD, bool RUNS>
 void launch_dkdv_docs(const BwdArgs &a, dim3 gr, hipStream_t s) {
   if (a.g.n_docs)
-    hipLaunchKernelGGL((dkdv_bf16_kernel<HD, MODE, RUNS, true>), gr, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((dkdv_bf16_kernel<HD, RUNS, true>), gr, dim3(NT), 0, s, a);
   else
-    hipLaunchKernelGGL((dkdv_bf16_kernel<HD, MODE, RUNS, false>), gr, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((dkdv_bf16_kernel<HD, RUNS, false>), gr, dim3(NT), 0, s, a);
 }
 
-template <int HD, int MODE>
-void launch_dkdv_variant(const BwdArgs &a, dim3 gr, hipStream_t s) {
-  if (a.runs)
-    launch_dkdv_docs<HD, MODE, true>(a, gr, s);
-  else
-    launch_dkdv_docs<HD, MODE, false>(a, gr, s);
-}
-
-hipError_t launch_bwd_dkdv_bf16(const BwdArgs &a, int hd, int64_t grid, int which, hipStream_t s) {
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (which != KV_DK && which != KV_DV) return hipErrorInvalidValue;
   const dim3 gr(static_cast<unsigned>(grid));
-  const bool dk = which == KV_DK;
   if (hd == 128) {
-    if (dk)
-      launch_dkdv_variant<128, KV_DK>(a, gr, s);
+    if (a.runs)
+      launch_dkdv_docs<128, true>(a, gr, s);
     else
-      launch_dkdv_variant<128, KV_DV>(a, gr, s);
+      launch_dkdv_docs<128, false>(a, gr, s);
   } else if (hd == 64) {
-    if (dk)
-      launch_dkdv_variant<64, KV_DK>(a, gr, s);
+    if (a.runs)
+      launch_dkdv_docs<64, true>(a, gr, s);
     else
-      launch_dkdv_variant<64, KV_DV>(a, gr, s);
+      launch_dkdv_docs<64, false>(a, gr, s);
   } else {
     return hipErrorInvalidValue;
   }

@@ -137,9 +137,10 @@ constexpr int kFwdWaves = 8;                // bf16 forward: waves per workgroup
 constexpr int kFwdTileQ = 32 * kFwdWaves;   // bf16 forward: query rows per workgroup
 constexpr int kFwdStages = 4;               // bf16 forward: K/V tiles resident in LDS
 constexpr int kBwdWaves = 8;                // bf16 dq, dk, dv: waves per workgroup
-constexpr int kBwdStages = 4;               // bf16 dq, dk, dv: tiles resident in LDS
+constexpr int kBwdStages = 4;               // bf16 dq: K/V tiles resident in LDS
 constexpr int kDqTileQ = 32 * kBwdWaves;    // bf16 dq: query rows per workgroup
 constexpr int kBwdTileKV = 32 * kBwdWaves;  // bf16 dk/dv: key rows per workgroup
+constexpr int kKvStages = 2;                // bf16 dk/dv: Q/dO tiles resident in LDS
 constexpr int kF32TileQ = 64;    // fp32 kernels: rows per workgroup
 constexpr int kF32TileKV = 64;
 
@@ -160,7 +161,7 @@ hipError_t launch_fwd_f32(const FwdArgs &a, int hd, int64_t grid, hipStream_t s)
 hipError_t launch_bwd_pre(const BwdArgs &a, int dtype, int hd, hipStream_t s);
 hipError_t launch_bwd_dq_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_t s);
 // which = 2: dK kernel, 1: dV kernel
-hipError_t launch_bwd_dkdv_bf16(const BwdArgs &a, int hd, int64_t grid, int which, hipStream_t s);
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_t s);
 hipError_t launch_bwd_dq_f32(const BwdArgs &a, int hd, int64_t grid, hipStream_t s);
 hipError_t launch_bwd_dkdv_f32(const BwdArgs &a, int hd, int64_t grid, hipStream_t s);
 // head_dim even, 2..512
