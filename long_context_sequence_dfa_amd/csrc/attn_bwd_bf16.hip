@@ -541,7 +541,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
         for (int ks = 0; ks < KS; ++ks)
           dpm = mfma32(__builtin_bit_cast(bf16x8, ld16(da + ks * 32)),
                        *reinterpret_cast<const bf16x8 *>(vpark + ks * 1024), dpm);
-        sched_lds_ahead<KS, 2>();
+        sched_lds_ahead<KS, 2, 2>();  // dO and V fragments
         __builtin_amdgcn_s_setprio(0);
         bf16x8 sb[2];
 #pragma unroll

@@ -124,15 +124,16 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Scheduling hint for a run of N LDS operand reads each feeding one of N
-// MFMAs: keep D reads in flight ahead of the products that consume them.
-template <int N, int D>
+// Scheduling hint for a run of N MFMAs, each fed by R LDS operand reads:
+// keep the reads of D products in flight ahead of the products that consume
+// them.
+template <int N, int D, int R = 1>
 __device__ __forceinline__ void sched_lds_ahead() {
-  __builtin_amdgcn_sched_group_barrier(0x100, D, 0);  // DS reads
+  __builtin_amdgcn_sched_group_barrier(0x100, D * R, 0);  // DS reads
 #pragma unroll
   for (int i = 0; i < N - D; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, D, 0);
 }
