@@ -171,10 +171,14 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
   }
   const int64_t lr = (static_cast<int64_t>(b) * G.hq + h) * G.seqlen + pos;
   const float lse2 = a.lse2[lr];
-  const float dd = a.dd[lr];
+  const float ndd = a.dd[lr];  // -D of this lane's row
   // the operands above and the first tiles have landed; from here on the only
   // vector-memory operations in flight are the tile loads
   vm_wait<0>();
+  // dP^T accumulations start from -D, so they end at dP - D directly
+  f32x16 nd;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) nd[i] = ndd;
 
   f32x16 acc[DT];
 #pragma unroll
@@ -222,7 +226,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {  // two halves of 32 keys
-        f32x16 sv = f32x16{}, pv = f32x16{};
+        f32x16 sv = f32x16{}, pv = nd;
         // the S/dP products at raised issue priority: while this wave feeds
         // the matrix core, the SIMD's other wave fills the VALU slots
         __builtin_amdgcn_s_setprio(1);
@@ -242,7 +246,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float pa = fast_exp2(__builtin_fmaf(sv[i], c, -lse2));
-          dsb[i / 8][i % 8] = static_cast<__bf16>(pa * (pv[i] - dd));
+          dsb[i / 8][i % 8] = static_cast<__bf16>(pa * pv[i]);
         }
         // dQ^T += K^T dS^T: A = K^T (d x 16 keys) read transposed from the K tile
 #pragma unroll
@@ -289,7 +293,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
   static_assert(TL::ROWS == KV_BQ, "query tiles are 64 rows");
   constexpr int RB = TL::RB;
   constexpr int TB = TL::TB;
-  constexpr int STAGE = 2 * TB + 2 * KV_BQ * 4;  // Q, dO, LSE*log2(e), D
+  constexpr int STAGE = 2 * TB + 2 * KV_BQ * 4;  // Q, dO, LSE*log2(e), -D
   constexpr int KS = HD / 16, DT = HD / 32;
   constexpr int VPARK = KS * 1024;               // parked V fragments per wave
   static_assert(KV_NS * STAGE + NW * VPARK <= 160 * 1024, "LDS budget");
@@ -390,7 +394,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
   first(gi, k, cw);
   int64_t t = cw.t0;
 
-  // Q/dO stream; LSE*log2(e) and D of the 64 rows go to LDS with one 4-byte
+  // Q/dO stream; LSE*log2(e) and -D of the 64 rows go to LDS with one 4-byte
   // direct load each, issued by the last two waves (they have the fewest
   // tile instructions)
   const TileStream<HD, NW> ld(wave, lane, 2 * G.qs[1] * rs, 2 * G.os[1] * rs);
@@ -534,8 +538,20 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
             accv[e] = mfma32(cat8(lds_read_tr(dt_ + o + 64 * e), lds_read_tr(dt_ + o + 4 * RB + 64 * e)),
                              pb[u], accv[e]);
         }
-        // dP = dO V^T, then dS = P (dP - D)
-        f32x16 dpm = f32x16{};
+        // dP = dO V^T, accumulated from -D (the tile's row statistics), so
+        // that dS = P (dP - D) is one product per element
+        f32x16 dpm;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int qoff = 32 * mt + 16 * u + 8 * g;
+          const f32x4 da4 = *reinterpret_cast<const f32x4 *>(ddt + qoff);
+          const f32x4 db4 = *reinterpret_cast<const f32x4 *>(ddt + qoff + 4);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            dpm[8 * u + w] = da4[w];
+            dpm[8 * u + 4 + w] = db4[w];
+          }
+        }
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -545,16 +561,9 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
         __builtin_amdgcn_s_setprio(0);
         bf16x8 sb[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int qoff = 32 * mt + 16 * u + 8 * g;
-          const f32x4 da4 = *reinterpret_cast<const f32x4 *>(ddt + qoff);
-          const f32x4 db4 = *reinterpret_cast<const f32x4 *>(ddt + qoff + 4);
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            const int i = 8 * u + w;
-            sb[u][w] = static_cast<__bf16>(s[i] * (dpm[i] - (w < 4 ? da4[w] : db4[w - 4])));
-          }
-        }
+          for (int w = 0; w < 8; ++w) sb[u][w] = static_cast<__bf16>(s[8 * u + w] * dpm[8 * u + w]);
         // dK^T += Q^T dS: A operand read transposed from the Q tile
 #pragma unroll
         for (int u = 0; u < 2; ++u) {

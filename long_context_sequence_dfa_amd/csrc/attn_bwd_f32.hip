@@ -102,7 +102,7 @@ __global__ __launch_bounds__(TQ) void dq_f32_kernel(BwdArgs a) {
           dp = fmaf(dov[c], vs[jj][c], dp);
         }
         const float p = expf(s * G.scale - lse);
-        const float ds = p * (dp - dd) * G.scale;
+        const float ds = p * (dp + dd) * G.scale;  // dd holds -D
 #pragma unroll
         for (int c = 0; c < HD; ++c) acc[c] = fmaf(ds, ks[jj][c], acc[c]);
       }
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(TK) void dkdv_f32_kernel(BwdArgs a) {
             dp = fmaf(ds_[ii][c], vv[c], dp);
           }
           const float p = expf(s * G.scale - ls_[ii]);
-          const float dsv = p * (dp - dd_[ii]) * G.scale;
+          const float dsv = p * (dp + dd_[ii]) * G.scale;  // dd_ holds -D
 #pragma unroll
           for (int c = 0; c < HD; ++c) {
             dk[c] = fmaf(dsv, qs_[ii][c], dk[c]);

@@ -117,7 +117,7 @@ struct BwdArgs {
   Geom g;
   const void *q, *k, *v, *o, *dout;
   const float *lse;  // [B][Hq][N]
-  float *dd;         // D = rowsum(dO*O): [B][Hq][N]
+  float *dd;         // -D = -rowsum(dO*O): [B][Hq][N]
   float *lse2;       // LSE * log2(e): [B][Hq][N]
   void *dq, *dk, *dv;
   const QSeg *qsegs;

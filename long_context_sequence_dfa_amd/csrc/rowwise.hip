@@ -1,5 +1,5 @@
 // rowwise.hip -- HBM-bound row kernels: accumulator init, log-sum-exp merge,
-// finalisation, zero fill and the backward's D = rowsum(dO * O).
+// finalisation, zero fill and the backward's D = rowsum(dO * O) (stored as -D).
 //
 // Merge rule (Striped Attention Guide, "Algorithmic Mechanics" 1, steps 4-7,
 // written for partials that are already normalised): with
@@ -88,7 +88,9 @@ __global__ __launch_bounds__(NT) void zero_rows_kernel(char *x, int64_t s0, int6
   if (lse && tid < rows) lse[tid] = -INFINITY;  // [B][H][N] has the same row count
 }
 
-// D[b][h][pos] = sum_c dO[b][pos][h][c] * O[b][pos][h][c]: one thread per row
+// -D[b][h][pos] = -sum_c dO[b][pos][h][c] * O[b][pos][h][c] (stored negated: the
+// gradient kernels start their dP accumulators from it) and LSE*log2(e): one
+// thread per row
 template <int HD, bool BF16>
 __global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdArgs a) {
   const Geom &G = a.g;
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) s = fmaf(ov[e], dv[e], s);
     }
   }
-  a.dd[tid] = s;
+  a.dd[tid] = -s;
   a.lse2[tid] = a.lse[tid] * kLog2e;
 }
 
