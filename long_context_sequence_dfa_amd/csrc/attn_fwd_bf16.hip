@@ -93,6 +93,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   constexpr int KS = HD / 16;       // MFMA k-steps over head_dim
   constexpr int DT = HD / 32;       // 32-row output tiles over head_dim
   constexpr float TAU = 8.f;        // lazy rescale threshold (log2 units)
+  constexpr float PSUM_MAX = 32768.f;  // unmasked tiles: largest accepted row-half sum of P
   __shared__ __attribute__((aligned(16))) char smem[NS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -171,6 +172,7 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
+  bool ref_ok = false;  // every row of the wave has a finite reference max
 
   // ---- tile sequence: (block k, tile t) over the blocks with visible keys ----
   const int nblk = TABLE ? seg.blk_count : 1;
@@ -253,7 +255,8 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
       // element i of s0 / s1 is key j0 + 32*(i/16) + 16*((i%16)/8) + 8g + i%8
       // (global position of key jj of the tile: gk + jj * rs)
       const int64_t gk = DOCS ? tile_pos(cw.kv_start, t) : 0;
-      if ((dw < BK - 1) || (j0 + BK > cw.len_kv) || (DOCS && gk < qlo_w)) {
+      const bool masked = (dw < BK - 1) || (j0 + BK > cw.len_kv) || (DOCS && gk < qlo_w);
+      if (masked) {
         // key j0 + jj is visible iff lo <= jj <= lim: lim from the causal
         // rule and the piece's end, lo from the row's document start
         const int64_t lim64 = c32 + dw;
@@ -285,36 +288,55 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
           }
         }
       }
-      // row max with the NaN-propagating maximum: v_maximum3_f32 needs no
-      // operand canonicalisation (the scores hold no NaN; -inf is kept)
-      float mx = __builtin_elementwise_maximum(s0[0], s1[0]);
-#pragma unroll
-      for (int i = 1; i < 16; ++i)
-        mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[i], s1[i]));
-      mx = pair_max(mx) * c;
-      // raise the reference max only when it grows by more than TAU: P <= 2^TAU
-      if (__any(mx > m_run + TAU)) {
-        const float m_new = __builtin_elementwise_maximum(m_run, mx);
-        // 1 for rows whose max did not rise (also all-masked rows: no -inf - -inf);
-        // 0 when a row sees its first key
-        const float alpha = m_new > m_run ? fast_exp2(m_run - m_new) : 1.f;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      // P = 2^(s c - m) with a per-row reference m.  Exact for any m (the
+      // output and the row sum share it); m only has to keep P in range.
+      // Tiles that need a mask, and every tile until all rows of the wave
+      // have a reference, take the full path: the tile's row max raises the
+      // reference when it grows by more than TAU, so P <= 2^TAU.  Otherwise
+      // P is formed against the current reference right away and the tile
+      // falls back to the full path only if some row half-sum exceeds
+      // PSUM_MAX (every P of it is then <= PSUM_MAX as well).
       float psum = 0.f;
       bf16x8 pb[4];
+      auto probs = [&](float m_use) {
+        psum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p0 = fast_exp2(__builtin_fmaf(s0[i], c, -m_use));
-        const float p1 = fast_exp2(__builtin_fmaf(s1[i], c, -m_use));
-        psum += p0 + p1;
-        pb[i / 8][i % 8] = static_cast<__bf16>(p0);
-        pb[2 + i / 8][i % 8] = static_cast<__bf16>(p1);
+        for (int i = 0; i < 16; ++i) {
+          const float p0 = fast_exp2(__builtin_fmaf(s0[i], c, -m_use));
+          const float p1 = fast_exp2(__builtin_fmaf(s1[i], c, -m_use));
+          psum += p0 + p1;
+          pb[i / 8][i % 8] = static_cast<__bf16>(p0);
+          pb[2 + i / 8][i % 8] = static_cast<__bf16>(p1);
+        }
+      };
+      bool full = masked || !ref_ok;
+      if (!full) {
+        probs(m_run);
+        full = __any(psum > PSUM_MAX);
+      }
+      if (full) {
+        // row max with the NaN-propagating maximum: v_maximum3_f32 needs no
+        // operand canonicalisation (the scores hold no NaN; -inf is kept)
+        float mx = __builtin_elementwise_maximum(s0[0], s1[0]);
+#pragma unroll
+        for (int i = 1; i < 16; ++i)
+          mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s0[i], s1[i]));
+        mx = pair_max(mx) * c;
+        // raise the reference max only when it grows by more than TAU
+        if (__any(mx > m_run + TAU)) {
+          const float m_new = __builtin_elementwise_maximum(m_run, mx);
+          // 1 for rows whose max did not rise (also all-masked rows: no -inf - -inf);
+          // 0 when a row sees its first key
+          const float alpha = m_new > m_run ? fast_exp2(m_run - m_new) : 1.f;
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+          m_run = m_new;
+        }
+        probs(m_run == -INFINITY ? 0.f : m_run);
+        ref_ok = !__any(m_run == -INFINITY);
       }
       l_run += psum;
       // O^T += V^T P^T: A = V^T (d x 16 keys) read transposed from the V tile
