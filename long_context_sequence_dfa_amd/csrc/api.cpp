@@ -3,11 +3,18 @@
 // launches on the caller's stream.
 //
 // Planning.  A block list is regrouped two ways:
-//  * by query piece (q_start, len_q, stride, run): each piece keeps its blocks in
-//    ring-step order -- the order in which a virtual rank receives key/value
-//    shards -- and is cut into query tiles (forward, dQ);
-//  * by key piece (kv_start, len_kv, stride, run): each keeps the blocks that read
-//    it, again in step order, cut into key tiles (dK, dV).
+//  * by query piece (q_start, len_q, stride, run): each piece keeps its blocks
+//    ordered by the key piece's first position (ring step breaks ties) and is
+//    cut into query tiles (forward, dQ);
+//  * by key piece (kv_start, len_kv, stride, run): each keeps the blocks that
+//    read it, ordered by the query piece's first position, cut into key tiles
+//    (dK, dV).
+// Fused kernels merge a row's blocks online, so their order changes only the
+// rounding, and a position order shared by every piece makes workgroups of
+// one head and of different virtual ranks that run side by side (similar
+// cost) read the same tiles at about the same time, from L2 (with stripe
+// blocks of 64 tokens the ring-step order left the L2 almost no reuse).
+// Stepwise mode keeps ring-step order (one launch per step).
 // Work tiles are sorted by decreasing cost so the heaviest start first.  The
 // tables travel to the device in the caller's workspace; the kernels read
 // key/value rows of the owning rank in place, so a ring step costs no copy
@@ -147,8 +154,8 @@ dfa_status plan_q(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n, in
   for (const auto &key : order) {
     auto idx = by_piece[key];
     std::stable_sort(idx.begin(), idx.end(), [&](int64_t a, int64_t b) {
-      return std::make_tuple(blocks[a].step, blocks[a].kv_start) <
-             std::make_tuple(blocks[b].step, blocks[b].kv_start);
+      return std::make_tuple(blocks[a].kv_start, blocks[a].step) <
+             std::make_tuple(blocks[b].kv_start, blocks[b].step);
     });
     QSeg s{};
     s.q_start = std::get<0>(key);
@@ -214,8 +221,8 @@ dfa_status plan_kv(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n, i
   for (const auto &key : order) {
     auto idx = by_piece[key];
     std::stable_sort(idx.begin(), idx.end(), [&](int64_t a, int64_t b) {
-      return std::make_tuple(blocks[a].step, blocks[a].q_start) <
-             std::make_tuple(blocks[b].step, blocks[b].q_start);
+      return std::make_tuple(blocks[a].q_start, blocks[a].step) <
+             std::make_tuple(blocks[b].q_start, blocks[b].step);
     });
     KvSeg s{};
     s.kv_start = std::get<0>(key);

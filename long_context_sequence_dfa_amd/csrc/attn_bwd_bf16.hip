@@ -9,7 +9,7 @@
 //
 // Two kernels, no atomics, deterministic (8 waves, 32 rows per wave):
 //  * dq: query-major, shaped like the forward -- a workgroup owns 256 query
-//    rows, walks its query piece's blocks in ring-step order and computes
+//    rows, walks its query piece's blocks in the host table's order and computes
 //    S^T = K Q^T, dP^T = V dO^T and dQ^T += K^T dS^T on the matrix cores.
 //    Each lane owns one query column, so LSE_i and D_i are per-lane scalars.
 //  * dkdv: key-major -- a workgroup owns 256 key rows, walks every block

@@ -1,9 +1,10 @@
 // attn_fwd_bf16.hip -- bf16 forward of blockwise causal attention on gfx950.
 //
 // One workgroup (8 waves) owns 256 query rows of one query piece, one batch
-// entry and one query head.  It walks the piece's blocks in ring-step order
-// (the key/value shard a virtual rank holds at each step, read in place) and,
-// inside each block, the 64-key tiles that hold at least one visible key.
+// entry and one query head.  It walks the piece's blocks (the key/value
+// shards a virtual rank holds over the ring steps, read in place) in the
+// order of the host's table and, inside each block, the 64-key tiles that
+// hold at least one visible key.
 // Per tile it keeps the running row max m, the running row sum l and the
 // running output O, rescaling by alpha = e^{m_old - m_new} (Striped Attention
 // Guide, "Algorithmic Mechanics" 1, steps 1-6), then normalises once at the

@@ -4,7 +4,7 @@
 // exactness to 1e-4 matters more than speed.  One workgroup of 64 threads
 // owns 64 query rows of a query piece; each thread owns one row and keeps its
 // running max, sum and output in registers while the workgroup streams
-// 64-key K/V tiles of the piece's blocks, in ring-step order, through LDS.
+// 64-key K/V tiles of the piece's blocks, in the host table's order, through LDS.
 // The update is the online-softmax rescaling of the Striped Attention Guide,
 // "Algorithmic Mechanics" 1, steps 1-7.  With packed documents a key is also
 // invisible when it lies before the first position of the query's document

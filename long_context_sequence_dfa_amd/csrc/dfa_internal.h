@@ -36,7 +36,7 @@ __host__ __device__ inline int64_t floor_div64(int64_t a, int64_t b) {
 }
 
 // One distinct query piece (rows as in piece_pos).  Its blocks (key pieces
-// in ring-step order) are kv[blk_begin, blk_begin + blk_count); the key
+// in position order) are kv[blk_begin, blk_begin + blk_count); the key
 // pieces share the query piece's stride and run.
 struct QSeg {
   int64_t q_start, len_q, stride, run;
