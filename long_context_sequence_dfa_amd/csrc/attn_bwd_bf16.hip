@@ -60,9 +60,10 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
   const Geom &G = a.g;
   const float c = G.scale_log2;
   const int BH = G.batch * G.hq;
-  const int64_t bid = blockIdx.x;
-  const int bh = static_cast<int>(bid % BH);
-  const Tile tl = ld_table(a.qtiles + bid / BH);
+  int bh;
+  int64_t ti;
+  if (!xcd_item(blockIdx.x, a.n_qtiles, BH, bh, ti)) return;
+  const Tile tl = ld_table(a.qtiles + ti);
   const QSeg seg = ld_table(a.qsegs + tl.seg);
   const int b = bh / G.hq, h = bh % G.hq, hk = h / G.group;
   const int64_t i0 = static_cast<int64_t>(tl.tile) * DQ_BQ;
@@ -305,7 +306,9 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
   const Geom &G = a.g;
   const float c = G.scale_log2;
   const int BH = G.batch * G.hkv;
+  // batch-head fastest: splitting the XCDs by head measured no faster here
   const int64_t bid = blockIdx.x;
+  if (bid >= static_cast<int64_t>(a.n_kvtiles) * BH) return;
   const int bh = static_cast<int>(bid % BH);
   const Tile tl = ld_table(a.kvtiles + bid / BH);
   const KvSeg seg = ld_table(a.kvsegs + tl.seg);
@@ -610,6 +613,7 @@ void launch_dq_variant(const BwdArgs &a, dim3 gr, hipStream_t s) {
 
 hipError_t launch_bwd_dq_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
+  grid = xcd_grid(grid);  // whole groups of 8 (see xcd_item)
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 gr(static_cast<unsigned>(grid));
   if (hd == 128) {

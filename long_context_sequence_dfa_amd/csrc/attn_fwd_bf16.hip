@@ -102,9 +102,9 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   const int g = lane >> 5, c32 = lane & 31;
   const Geom &G = a.g;
   const int BH = G.batch * G.hq;
-  const int64_t bid = blockIdx.x;
-  const int bh = static_cast<int>(bid % BH);
-  const int64_t ti = bid / BH;
+  int bh;
+  int64_t ti;
+  if (!xcd_item(blockIdx.x, TABLE ? a.n_tiles : (a.seg0.len_q + BQ - 1) / BQ, BH, bh, ti)) return;
   const int b = bh / G.hq, h = bh % G.hq, hk = h / G.group;
 
   QSeg seg;
@@ -437,6 +437,7 @@ void launch_fwd_variant(const FwdArgs &a, dim3 gr, hipStream_t s) {
 
 hipError_t launch_fwd_bf16(const FwdArgs &a, int hd, int64_t grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
+  grid = xcd_grid(grid);  // whole groups of 8 (see xcd_item)
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (a.out_mode != 1 && !a.segs) return hipErrorInvalidValue;
   const dim3 gr(static_cast<unsigned>(grid));

@@ -110,6 +110,32 @@ __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<
 __device__ __forceinline__ void st16(void *p, u32x4 v) { *reinterpret_cast<u32x4 *>(p) = v; }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Work item (batch-head, work tile) of workgroup `bid` when n = n_tiles * BH
+// items run on a grid of xcd_grid(n) workgroups; work tiles come sorted by
+// decreasing cost.  Workgroup i is dispatched to XCD i mod 8, and each XCD
+// has its own L2.  With BH a multiple of 8, XCD x takes the BH / 8 whole
+// batch-heads x BH / 8 .. (x + 1) BH / 8 - 1, one after the other, each tile
+// by tile: the workgroups an XCD runs side by side then share one head and
+// read its K/V (or Q/dO) tiles from that L2, and every XCD gets the same mix
+// of costs.  Otherwise items go out with the batch-head fastest (an XCD
+// split by heads would leave some XCDs only the costly tiles).  False for
+// padding workgroups.
+__device__ __forceinline__ bool xcd_item(int64_t bid, int64_t n_tiles, int BH, int &bh, int64_t &tile) {
+  const int64_t n = n_tiles * BH;
+  if (BH % 8 == 0) {
+    const int64_t i = (bid & 7) * (n / 8) + (bid >> 3);
+    bh = static_cast<int>(i / n_tiles);
+    tile = i - static_cast<int64_t>(bh) * n_tiles;
+    return true;  // the grid is exactly n workgroups
+  }
+  if (bid >= n) return false;
+  bh = static_cast<int>(bid % BH);
+  tile = bid / BH;
+  return true;
+}
+// Grid size for n items mapped by xcd_item: 8 ceil(n / 8).
+inline int64_t xcd_grid(int64_t n) { return (n + 7) / 8 * 8; }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // max / sum over the lane pair (l, l ^ 32), returned in both lanes: one
