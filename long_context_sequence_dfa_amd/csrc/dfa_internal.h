@@ -160,7 +160,9 @@ hipError_t launch_fwd_bf16(const FwdArgs &a, int hd, int64_t grid, hipStream_t s
 hipError_t launch_fwd_f32(const FwdArgs &a, int hd, int64_t grid, hipStream_t s);
 hipError_t launch_bwd_pre(const BwdArgs &a, int dtype, int hd, hipStream_t s);
 hipError_t launch_bwd_dq_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_t s);
-// which = 2: dK kernel, 1: dV kernel
+// grid: work items (tiles x batch-heads); the bf16 forward and dQ launchers
+// round it up to whole groups of 8 (xcd_item); the dK/dV kernel writes both
+// gradients
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_t s);
 hipError_t launch_bwd_dq_f32(const BwdArgs &a, int hd, int64_t grid, hipStream_t s);
 hipError_t launch_bwd_dkdv_f32(const BwdArgs &a, int hd, int64_t grid, hipStream_t s);
