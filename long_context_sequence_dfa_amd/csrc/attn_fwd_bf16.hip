@@ -104,7 +104,17 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   const int BH = G.batch * G.hq;
   int bh;
   int64_t ti;
-  if (!xcd_item(blockIdx.x, TABLE ? a.n_tiles : (a.seg0.len_q + BQ - 1) / BQ, BH, bh, ti)) return;
+  if constexpr (OUT == 0) {
+    if (!xcd_item(blockIdx.x, a.n_tiles, BH, bh, ti)) return;
+  } else {
+    // per-step partials: batch-head fastest measured faster (in one ring
+    // step every virtual rank reads another shard, so an XCD's workgroups
+    // share no K/V whichever way they are grouped)
+    const int64_t bid = blockIdx.x;
+    if (bid >= (TABLE ? a.n_tiles : (a.seg0.len_q + BQ - 1) / BQ) * static_cast<int64_t>(BH)) return;
+    bh = static_cast<int>(bid % BH);
+    ti = bid / BH;
+  }
   const int b = bh / G.hq, h = bh % G.hq, hk = h / G.group;
 
   QSeg seg;
