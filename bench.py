@@ -186,7 +186,7 @@ def main() -> int:
                     help="run one 1 GiB device copy first (scale for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus "
               f"{args.gpus}); the schedules run as virtual ranks on one device.", file=sys.stderr)
         return 2
 
