@@ -189,6 +189,25 @@ dfa_status plan_q(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n, in
   return DFA_OK;
 }
 
+// The fused query-major walks (forward, dQ) interleave a piece's blocks in
+// groups of kIlvTiles key tiles when every block is a near-triangle over
+// single-token rows (|diag_offset| <= 1, run = 1: token striping), so that
+// the query tiles of one head, whose costs differ, read the same key tiles
+// at about the same time (from L2; the HBM traffic saved raises the clock);
+// the kernels then keep one block per lane (at most 64 per piece, 32-bit
+// lengths).  Other schedules keep the walk block after block: with stripe
+// blocks of 64-128 tokens the position-ordered walk already shares L2 and
+// the interleave's cursor measured slower.
+bool interleavable(const dfa_block *blocks, int64_t n, const QPlan &qp) {
+  for (int64_t i = 0; i < n; ++i)
+    if (blocks[i].diag_offset < -1 || blocks[i].diag_offset > 1 || blocks[i].len_kv > INT32_MAX ||
+        blocks[i].run != 1)
+      return false;
+  for (const auto &s : qp.segs)
+    if (s.blk_count > 64) return false;
+  return true;
+}
+
 // ---- key-major plan (dK, dV) ----
 struct KvPlan {
   std::vector<KvSeg> segs;
@@ -616,6 +635,7 @@ extern "C" dfa_status dfa_attn_fwd(const dfa_attn_desc *d, const dfa_block *bloc
     a.o = o;
     a.lse = lse;
     a.out_mode = 0;
+    a.interleave = interleavable(blocks, n_blocks, qp);
     a.segs = reinterpret_cast<const QSeg *>(ws + L.segs);
     a.kv = reinterpret_cast<const KvRef *>(ws + L.kv);
     a.tiles = reinterpret_cast<const Tile *>(ws + L.tiles);
@@ -741,6 +761,7 @@ extern "C" dfa_status dfa_attn_bwd_ex(const dfa_attn_desc *d, const dfa_block *b
   a.qkv = reinterpret_cast<const KvRef *>(ws + L.qkv);
   a.qtiles = reinterpret_cast<const Tile *>(ws + L.qtiles);
   a.n_qtiles = static_cast<int32_t>(qp.tiles.size());
+  a.interleave = interleavable(blocks, n_blocks, qp);
   a.kvsegs = reinterpret_cast<const KvSeg *>(ws + L.kvsegs);
   a.kvq = reinterpret_cast<const QRef *>(ws + L.kvq);
   a.kvtiles = reinterpret_cast<const Tile *>(ws + L.kvtiles);

@@ -46,7 +46,8 @@ static_assert(DQ_BQ == 32 * NW, "one 32-query column block per wave");
 
 // RUNS: pieces made of runs (stripe blocks), visibility from global
 // positions; otherwise rows start + i*stride and each block's diagonal.
-template <int HD, bool RUNS, bool DOCS>
+// ILV: the interleaved walk (groups of kIlvTiles key tiles, as in the forward).
+template <int HD, bool RUNS, bool DOCS, bool ILV>
 __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
   using TL = Tile64<HD>;
   static_assert(TL::ROWS == DQ_BK, "key tiles are 64 rows");
@@ -103,10 +104,9 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
 
   // walk over (block, key tile); t0 skips tiles before wlo
   struct Walk {
-    int64_t kv_start, len_kv, diag, ntiles, t0;
+    int64_t kv_start, len_kv, diag, ntiles, t0, te;
   };
-  auto walk = [&](int k) {  // key tiles holding a key at or before the last row
-    const KvRef r = ld_table(a.qkv + seg.blk_begin + k);
+  auto walk_of = [&](const KvRef &r) {  // key tiles holding a key at or before the last row
     int64_t hi;
     if constexpr (RUNS) {
       hi = piece_count_le(r.kv_start, seg.stride, seg.run, r.len_kv, q_last);
@@ -115,9 +115,41 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
       if (hi > r.len_kv) hi = r.len_kv;
     }
     const int64_t t0 = wlo > 0 ? piece_count_le(r.kv_start, seg.stride, seg.run, r.len_kv, wlo - 1) / DQ_BK : 0;
-    return Walk{r.kv_start, r.len_kv, r.diag_offset, hi > 0 ? (hi + DQ_BK - 1) / DQ_BK : 0, t0};
+    const int64_t nt = hi > 0 ? (hi + DQ_BK - 1) / DQ_BK : 0;
+    return Walk{r.kv_start, r.len_kv, r.diag_offset, nt, t0, nt};
   };
+  auto walk = [&](int k) { return walk_of(ld_table(a.qkv + seg.blk_begin + k)); };
   const int nblk = seg.blk_count;
+  // Interleaved (the host's choice when every block is a near-triangle, as
+  // under striping): tiles [g, g + G) of every block, then [g + G, g + 2G),
+  // G = kIlvTiles.  The query tiles of one head that run side by side on an
+  // XCD then read key tiles of one narrow window (from L2, a few MB) whatever
+  // their row ranges, where walking block after block spread them over
+  // every block and sent each read to HBM; G > 1 keeps the cursor's block
+  // switch off most tiles.  Lane l holds block l's walk (at most 64 blocks).
+  static_assert((kIlvTiles & (kIlvTiles - 1)) == 0, "group size: a power of two");
+  int64_t iw_kv = 0;
+  int32_t iw_len = 0, iw_diag = 0, iw_nt = 0, iw_t0 = 0, ilv_tend = 0;
+  int64_t ilv_tbeg = 0;
+  if constexpr (ILV) {
+    if (lane < nblk) {
+      const auto w = walk_of(a.qkv[seg.blk_begin + lane]);
+      iw_kv = w.kv_start;
+      iw_len = static_cast<int32_t>(w.len_kv);
+      iw_diag = static_cast<int32_t>(w.diag);
+      iw_nt = static_cast<int32_t>(w.ntiles);
+      iw_t0 = static_cast<int32_t>(w.t0);
+    }
+    int32_t tb = 0x7fffffff;
+    for (int l = 0; l < nblk; ++l) {
+      const int32_t nt = __builtin_amdgcn_readlane(iw_nt, l), t0 = __builtin_amdgcn_readlane(iw_t0, l);
+      if (nt > t0) {
+        ilv_tend = nt > ilv_tend ? nt : ilv_tend;
+        tb = t0 < tb ? t0 : tb;
+      }
+    }
+    ilv_tbeg = tb & ~static_cast<int64_t>(kIlvTiles - 1);
+  }
   auto first = [&](int &k_, Walk &w_) {
     while (k_ < nblk) {
       w_ = walk(k_);
@@ -126,15 +158,55 @@ __global__ __launch_bounds__(NT, 8 / NW) void dq_bf16_kernel(BwdArgs a) {
     }
   };
   auto next = [&](int &k_, int64_t &t_, Walk &w_) {
+    if constexpr (ILV) {
+      if (++t_ < w_.te) return;
+      // next block of the group, or the first block of the next group; the
+      // group start moves once per pass over the blocks, ending at ilv_tend
+      int64_t g = (t_ - 1) & ~static_cast<int64_t>(kIlvTiles - 1);
+      for (;;) {
+        if (++k_ >= nblk) {
+          k_ = 0;
+          g += kIlvTiles;
+          if (g >= ilv_tend) {
+            k_ = nblk;
+            return;
+          }
+        }
+        const int32_t nt = __builtin_amdgcn_readlane(iw_nt, k_);
+        const int32_t t0 = __builtin_amdgcn_readlane(iw_t0, k_);
+        const int64_t tb = g > t0 ? g : t0;
+        const int64_t te = g + kIlvTiles < nt ? g + kIlvTiles : nt;
+        if (tb < te) {
+          w_.kv_start = readlane64(iw_kv, k_);
+          w_.len_kv = __builtin_amdgcn_readlane(iw_len, k_);
+          w_.diag = __builtin_amdgcn_readlane(iw_diag, k_);
+          w_.ntiles = nt;
+          w_.t0 = t0;
+          w_.te = te;
+          t_ = tb;
+          return;
+        }
+      }
+    }
     if (++t_ < w_.ntiles) return;
     ++k_;
     first(k_, w_);
     t_ = w_.t0;
   };
   int k = 0;
-  Walk cw{0, 0, 0, 0, 0};
-  first(k, cw);
-  int64_t t = cw.t0;
+  Walk cw{0, 0, 0, 0, 0, 0};
+  int64_t t;
+  if constexpr (ILV) {
+    // one step before block 0's tiles of the first group (k = nblk - 1 wraps
+    // to block 0 of group ilv_tbeg); nothing visible: ilv_tbeg >= ilv_tend
+    k = nblk - 1;
+    t = ilv_tbeg - kIlvTiles;
+    cw.te = t + 1;
+    next(k, t, cw);
+  } else {
+    first(k, cw);
+    t = cw.t0;
+  }
 
   // K and V stream
   const TileStream<HD, NW> ld(wave, lane, 2 * G.ks[1] * rs, 2 * G.vs[1] * rs);
@@ -605,10 +677,14 @@ __global__ __launch_bounds__(NT, 8 / NW) void dkdv_bf16_kernel(BwdArgs a) {
 
 template <int HD, bool RUNS>
 void launch_dq_variant(const BwdArgs &a, dim3 gr, hipStream_t s) {
-  if (a.g.n_docs)
-    hipLaunchKernelGGL((dq_bf16_kernel<HD, RUNS, true>), gr, dim3(NT), 0, s, a);
+  if (a.g.n_docs && a.interleave)
+    hipLaunchKernelGGL((dq_bf16_kernel<HD, RUNS, true, true>), gr, dim3(NT), 0, s, a);
+  else if (a.g.n_docs)
+    hipLaunchKernelGGL((dq_bf16_kernel<HD, RUNS, true, false>), gr, dim3(NT), 0, s, a);
+  else if (a.interleave)
+    hipLaunchKernelGGL((dq_bf16_kernel<HD, RUNS, false, true>), gr, dim3(NT), 0, s, a);
   else
-    hipLaunchKernelGGL((dq_bf16_kernel<HD, RUNS, false>), gr, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL((dq_bf16_kernel<HD, RUNS, false, false>), gr, dim3(NT), 0, s, a);
 }
 
 hipError_t launch_bwd_dq_bf16(const BwdArgs &a, int hd, int64_t grid, hipStream_t s) {

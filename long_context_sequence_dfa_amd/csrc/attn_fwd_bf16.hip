@@ -51,6 +51,7 @@ static_assert(BQ == 32 * NW, "one 32-query column block per wave");
 struct BlockWalk {
   int64_t kv_start, len_kv, diag, ntiles;
   int64_t t0;  // first tile with a key visible to some row (packed documents)
+  int64_t te;  // interleaved walk: end of the current group's tiles of this block
 };
 
 // The key piece of block k; ntiles covers every key at or before the
@@ -59,14 +60,9 @@ struct BlockWalk {
 // (0 without packed documents).  RUNS: pieces made of runs (stripe blocks),
 // visibility from global positions; otherwise rows start + i*stride and the
 // block's diagonal.
-template <bool TABLE, bool RUNS>
-__device__ __forceinline__ BlockWalk block_walk(const FwdArgs &a, const QSeg &seg, int k,
-                                                int64_t iend, int64_t q_last, int64_t wlo) {
-  KvRef r;
-  if constexpr (TABLE)
-    r = ld_table(a.kv + seg.blk_begin + k);
-  else
-    r = a.kv0;
+template <bool RUNS>
+__device__ __forceinline__ BlockWalk walk_of(const KvRef &r, const QSeg &seg, int64_t iend,
+                                             int64_t q_last, int64_t wlo) {
   BlockWalk w;
   w.kv_start = r.kv_start;
   w.len_kv = r.len_kv;
@@ -80,12 +76,25 @@ __device__ __forceinline__ BlockWalk block_walk(const FwdArgs &a, const QSeg &se
   }
   w.ntiles = hi > 0 ? (hi + BK - 1) / BK : 0;
   w.t0 = wlo > 0 ? piece_count_le(r.kv_start, seg.stride, seg.run, r.len_kv, wlo - 1) / BK : 0;
+  w.te = w.ntiles;
   return w;
+}
+
+template <bool TABLE, bool RUNS>
+__device__ __forceinline__ BlockWalk block_walk(const FwdArgs &a, const QSeg &seg, int k,
+                                                int64_t iend, int64_t q_last, int64_t wlo) {
+  KvRef r;
+  if constexpr (TABLE)
+    r = ld_table(a.kv + seg.blk_begin + k);
+  else
+    r = a.kv0;
+  return walk_of<RUNS>(r, seg, iend, q_last, wlo);
 }
 
 // TABLE: the query piece and its blocks come from the work tables (fused and
 // stepwise walks); otherwise from seg0/kv0 (one block).
-template <int HD, int OUT, bool TABLE, bool RUNS, bool DOCS>
+// ILV: the interleaved walk (fused mode only).
+template <int HD, int OUT, bool TABLE, bool RUNS, bool DOCS, bool ILV = false>
 __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
   using TL = Tile64<HD>;
   static_assert(TL::ROWS == BK, "key tiles are 64 rows");
@@ -187,6 +196,36 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
 
   // ---- tile sequence: (block k, tile t) over the blocks with visible keys ----
   const int nblk = TABLE ? seg.blk_count : 1;
+  // Interleaved (the host's choice when every block is a near-triangle, as
+  // under striping): tiles [g, g + G) of every block, then [g + G, g + 2G),
+  // G = kIlvTiles.  The query tiles of one head that run side by side on an
+  // XCD then read key tiles of one narrow window (from L2, a few MB) whatever
+  // their row ranges, where walking block after block spread them over
+  // every block and sent each read to HBM; G > 1 keeps the cursor's block
+  // switch off most tiles.  Lane l holds block l's walk (at most 64 blocks).
+  static_assert((kIlvTiles & (kIlvTiles - 1)) == 0, "group size: a power of two");
+  int64_t iw_kv = 0;
+  int32_t iw_len = 0, iw_diag = 0, iw_nt = 0, iw_t0 = 0, ilv_tend = 0;
+  int64_t ilv_tbeg = 0;
+  if constexpr (ILV) {
+    if (lane < nblk) {
+      const auto w = walk_of<RUNS>(a.kv[seg.blk_begin + lane], seg, iend, q_last, wlo);
+      iw_kv = w.kv_start;
+      iw_len = static_cast<int32_t>(w.len_kv);
+      iw_diag = static_cast<int32_t>(w.diag);
+      iw_nt = static_cast<int32_t>(w.ntiles);
+      iw_t0 = static_cast<int32_t>(w.t0);
+    }
+    int32_t tb = 0x7fffffff;
+    for (int l = 0; l < nblk; ++l) {
+      const int32_t nt = __builtin_amdgcn_readlane(iw_nt, l), t0 = __builtin_amdgcn_readlane(iw_t0, l);
+      if (nt > t0) {
+        ilv_tend = nt > ilv_tend ? nt : ilv_tend;
+        tb = t0 < tb ? t0 : tb;
+      }
+    }
+    ilv_tbeg = tb & ~static_cast<int64_t>(kIlvTiles - 1);
+  }
   auto first = [&](int &k_, BlockWalk &w_) {
     while (k_ < nblk) {
       w_ = block_walk<TABLE, RUNS>(a, seg, k_, iend, q_last, wlo);
@@ -195,15 +234,55 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
     }
   };
   auto next = [&](int &k_, int64_t &t_, BlockWalk &w_) {
+    if constexpr (ILV) {
+      if (++t_ < w_.te) return;
+      // next block of the group, or the first block of the next group; the
+      // group start moves once per pass over the blocks, ending at ilv_tend
+      int64_t g = (t_ - 1) & ~static_cast<int64_t>(kIlvTiles - 1);
+      for (;;) {
+        if (++k_ >= nblk) {
+          k_ = 0;
+          g += kIlvTiles;
+          if (g >= ilv_tend) {
+            k_ = nblk;
+            return;
+          }
+        }
+        const int32_t nt = __builtin_amdgcn_readlane(iw_nt, k_);
+        const int32_t t0 = __builtin_amdgcn_readlane(iw_t0, k_);
+        const int64_t tb = g > t0 ? g : t0;
+        const int64_t te = g + kIlvTiles < nt ? g + kIlvTiles : nt;
+        if (tb < te) {
+          w_.kv_start = readlane64(iw_kv, k_);
+          w_.len_kv = __builtin_amdgcn_readlane(iw_len, k_);
+          w_.diag = __builtin_amdgcn_readlane(iw_diag, k_);
+          w_.ntiles = nt;
+          w_.t0 = t0;
+          w_.te = te;
+          t_ = tb;
+          return;
+        }
+      }
+    }
     if (++t_ < w_.ntiles) return;
     ++k_;
     first(k_, w_);
     t_ = w_.t0;
   };
   int k = 0;
-  BlockWalk cw{0, 0, 0, 0, 0};
-  first(k, cw);
-  int64_t t = cw.t0;
+  BlockWalk cw{0, 0, 0, 0, 0, 0};
+  int64_t t;
+  if constexpr (ILV) {
+    // one step before block 0's tiles of the first group (k = nblk - 1 wraps
+    // to block 0 of group ilv_tbeg); nothing visible: ilv_tbeg >= ilv_tend
+    k = nblk - 1;
+    t = ilv_tbeg - kIlvTiles;
+    cw.te = t + 1;
+    next(k, t, cw);
+  } else {
+    first(k, cw);
+    t = cw.t0;
+  }
 
   // ---- K/V stream: NS LDS stages, the load cursor runs NS - 1 tiles ahead ----
   const TileStream<HD, NW> ld(wave, lane, 2 * G.ks[1] * rs, 2 * G.vs[1] * rs);
@@ -427,7 +506,9 @@ __global__ __launch_bounds__(NT, 8 / NW) void fwd_bf16_kernel(FwdArgs a) {
 template <int HD, bool RUNS, bool DOCS>
 void launch_fwd_docs(const FwdArgs &a, dim3 gr, hipStream_t s) {
   const dim3 bl(NT);
-  if (a.out_mode == 0)
+  if (a.out_mode == 0 && a.interleave)
+    hipLaunchKernelGGL((fwd_bf16_kernel<HD, 0, true, RUNS, DOCS, true>), gr, bl, 0, s, a);
+  else if (a.out_mode == 0)
     hipLaunchKernelGGL((fwd_bf16_kernel<HD, 0, true, RUNS, DOCS>), gr, bl, 0, s, a);
   else if (a.out_mode == 2)
     hipLaunchKernelGGL((fwd_bf16_kernel<HD, 2, true, RUNS, DOCS>), gr, bl, 0, s, a);

@@ -45,6 +45,13 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t x) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// Lane `l` (wave-uniform) of a 64-bit value.
+__device__ __forceinline__ int64_t readlane64(int64_t x, int l) {
+  const unsigned lo = __builtin_amdgcn_readlane(static_cast<unsigned>(x), l);
+  const unsigned hi = __builtin_amdgcn_readlane(static_cast<unsigned>(static_cast<uint64_t>(x) >> 32), l);
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Read of a work-table entry (wave-uniform address, constant for the whole
 // launch) with scalar loads (early-clobber outputs: the second load of a
 // pair still reads the base).  Written as inline assembly so that it stays a

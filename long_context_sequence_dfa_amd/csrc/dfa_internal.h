@@ -108,6 +108,9 @@ struct FwdArgs {
                      // 2: partials merged into the accumulator rows (rows of one
                      // launch are distinct)
   int32_t runs;      // some piece is made of runs (run > 1)
+  int32_t interleave;  // fused walk in groups of kIlvTiles key tiles per block, block after
+                       // block, group after group (every block a near-triangle:
+                       // |diag_offset| <= 1, len_kv < 2^31, at most 64 blocks per piece)
   QSeg seg0;         // used when segs == nullptr (one block, no table)
   KvRef kv0;
 };
@@ -129,6 +132,7 @@ struct BwdArgs {
   const Tile *kvtiles;
   int32_t n_kvtiles;
   int32_t runs;  // some piece is made of runs (run > 1)
+  int32_t interleave;  // dQ walk as FwdArgs::interleave
 };
 
 
@@ -141,6 +145,7 @@ constexpr int kBwdStages = 4;               // bf16 dq: K/V tiles resident in LD
 constexpr int kDqTileQ = 32 * kBwdWaves;    // bf16 dq: query rows per workgroup
 constexpr int kBwdTileKV = 32 * kBwdWaves;  // bf16 dk/dv: key rows per workgroup
 constexpr int kKvStages = 2;                // bf16 dk/dv: Q/dO tiles resident in LDS
+constexpr int kIlvTiles = 4;      // interleaved walks: key tiles per block and group (2^k)
 constexpr int kF32TileQ = 64;    // fp32 kernels: rows per workgroup
 constexpr int kF32TileKV = 64;
 
