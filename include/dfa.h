@@ -145,7 +145,8 @@ typedef struct dfa_attn_desc {
   int32_t heads_q;       /* >= 1 */
   int32_t heads_kv;      /* >= 1, divides heads_q */
   int32_t head_dim;      /* 64 or 128 */
-  float softmax_scale;   /* the caller passes 1/sqrt(head_dim) for standard attention */
+  float softmax_scale;   /* finite and > 0, else DFA_E_SHAPE; the caller passes
+                            1/sqrt(head_dim) for standard attention */
   int64_t seqlen;        /* global N; every pointer indexes global token order */
   int64_t q_strides[3];
   int64_t k_strides[3];
@@ -224,7 +225,8 @@ dfa_status dfa_schedule_balance(const dfa_block *blocks, int64_t n_blocks, int32
  *              is the block's query row i normalised over the block's visible
  *              keys only.
  *   lse_part : device fp32 [batch][heads_q][len_q]; LSE of those keys.
- * A row with no visible key gets O = 0 and LSE = -inf.
+ * A row with no visible key gets O = 0 and LSE = -inf.  bf16: the 2^31-byte
+ * limit on 64 rows of k and v of dfa_attn_fwd applies.
  */
 dfa_status dfa_attn_block_fwd(const dfa_attn_desc *d, const dfa_block *blk, const void *q,
                               const void *k, const void *v, float *o_part, float *lse_part,
@@ -244,7 +246,13 @@ dfa_status dfa_lse_merge(int64_t n_rows, int32_t head_dim, float *o_acc, float *
 
 /*
  * dfa_attn_fwd -- forward over a block list (a whole schedule or any subset,
- * e.g. one rank's share).
+ * e.g. one rank's share): exact causal attention of every query row over the
+ * keys its blocks give it, O = softmax(scale Q K^T) V per row with the
+ * running max / sum / output of the online softmax and LSE = m + ln l
+ * (Striped Attention Guide, "Algorithmic Mechanics" 1, steps 1-7; the page's
+ * opening of "Algorithmic Mechanics" states that the result is exact, equal to
+ * one monolithic attention pass, as does the FlashAttention glossary page,
+ * first two paragraphs).
  *   blocks/n_blocks : host array (as built by dfa_schedule_build or a subset).
  *                     The distinct query pieces (q_start, len_q, stride, run) must
  *                     not share rows, nor the distinct key pieces.
@@ -254,6 +262,9 @@ dfa_status dfa_lse_merge(int64_t n_rows, int32_t head_dim, float *o_acc, float *
  *   workspace       : device buffer of at least dfa_workspace_size() bytes,
  *                     256-byte aligned (may be NULL if that size is 0).
  * Output rows that no block touches are written as O = 0, LSE = -inf.
+ * bf16: 64 consecutive rows of one piece must span less than 2^31 bytes in
+ * each of k and v (64 * 2 * token stride * row step, the row step being the
+ * block's stride for run = 1 and 1 otherwise), else DFA_E_UNSUPPORTED.
  */
 dfa_status dfa_attn_fwd(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n_blocks,
                         int32_t mode, const void *q, const void *k, const void *v, void *o,
@@ -261,7 +272,12 @@ dfa_status dfa_attn_fwd(const dfa_attn_desc *d, const dfa_block *blocks, int64_t
 
 /*
  * dfa_attn_bwd -- gradients of the forward over the same block list:
- * dS = P (dP - D) with P recomputed from the saved LSE and D = rowsum(dO*O).
+ * dS = P (dP - D) with P recomputed from the saved LSE and D = rowsum(dO*O)
+ * (the backward keeps only O and the per-row statistics and recomputes the
+ * attention matrix: FlashAttention glossary page, first two paragraphs;
+ * DistFlashAttn paper record, "rematerialisation-aware gradient
+ * checkpointing").  The gradient formulas are the vector-Jacobian product of
+ * the forward's definition; the pages give none.
  *   o, lse      : the forward's outputs for the same block list.
  *   dq, dk, dv  : device, dtype, strides of q, k, v.  Overwritten; rows no
  *                 block touches are written as 0.  For grouped-query

@@ -25,6 +25,7 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <initializer_list>
 #include <map>
 #include <tuple>
 #include <vector>
@@ -59,7 +60,9 @@ dfa_status check_desc(const dfa_attn_desc *d) {
   if (d->head_dim != 64 && d->head_dim != 128) return DFA_E_UNSUPPORTED;
   if (d->batch < 1 || d->heads_q < 1 || d->heads_kv < 1 || d->seqlen < 1) return DFA_E_SHAPE;
   if (d->heads_q % d->heads_kv) return DFA_E_SHAPE;
-  if (!std::isfinite(d->softmax_scale)) return DFA_E_SHAPE;
+  // the kernels take each row's maximum of scale * q.k as its reference:
+  // that is the largest score only for a positive scale
+  if (!std::isfinite(d->softmax_scale) || !(d->softmax_scale > 0.f)) return DFA_E_SHAPE;
   if (d->doc_bounds && (d->n_docs < 1 || d->n_docs > d->seqlen || d->seqlen > INT32_MAX))
     return DFA_E_SHAPE;
   const int64_t elems16 = d->dtype == DFA_BF16 ? 8 : 4;  // elements per 16 bytes
@@ -93,6 +96,24 @@ dfa_status check_block(const dfa_attn_desc *d, const dfa_block &b) {
     return DFA_E_SHAPE;
   // the block's run-level offset (for run = 1 the exact mask rule)
   if (b.diag_offset != floor_div(b.q_start - b.kv_start, b.stride)) return DFA_E_SHAPE;
+  return DFA_OK;
+}
+
+// The bf16 kernels stream 64-row tiles of a piece into LDS with 32-bit byte
+// offsets from the tile's first row: 64 rows (token stride times the row step
+// inside a tile) must span less than 2^31 bytes in every streamed tensor.
+dfa_status check_tile_span(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n,
+                           std::initializer_list<int64_t> token_strides) {
+  if (d->dtype != DFA_BF16) return DFA_OK;
+  int64_t row_elems = 0;
+  for (int64_t s : token_strides) row_elems = std::max(row_elems, s);
+  const int64_t limit = (int64_t{1} << 31) / 64;
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t step = dfa::piece_row_step(blocks[i].stride, blocks[i].run);
+    // 2 * row_elems * step >= limit, without overflow for any int64 inputs
+    if (row_elems >= limit || step >= limit || 2 * row_elems >= (limit + step - 1) / step)
+      return DFA_E_UNSUPPORTED;
+  }
   return DFA_OK;
 }
 
@@ -557,6 +578,8 @@ extern "C" dfa_status dfa_attn_block_fwd(const dfa_attn_desc *d, const dfa_block
   if (st != DFA_OK) return st;
   if (!ptr_aligned(q) || !ptr_aligned(k) || !ptr_aligned(v) || !ptr_aligned(o_part))
     return DFA_E_ALIGN;
+  st = check_tile_span(d, blk, 1, {d->k_strides[1], d->v_strides[1]});
+  if (st != DFA_OK) return st;
   dfa::FwdArgs a{};
   a.g = make_geom(d);
   a.q = q;
@@ -597,6 +620,8 @@ extern "C" dfa_status dfa_attn_fwd(const dfa_attn_desc *d, const dfa_block *bloc
   if (!ptr_aligned(q) || !ptr_aligned(k) || !ptr_aligned(v) || !ptr_aligned(o)) return DFA_E_ALIGN;
   if (mode != DFA_FWD_FUSED && mode != DFA_FWD_STEPWISE) return DFA_E_UNSUPPORTED;
   st = check_blocks(d, blocks, n_blocks);
+  if (st != DFA_OK) return st;
+  st = check_tile_span(d, blocks, n_blocks, {d->k_strides[1], d->v_strides[1]});
   if (st != DFA_OK) return st;
   QPlan qp;
   st = plan_q(d, blocks, n_blocks, fwd_tile(d), qp);
@@ -700,14 +725,10 @@ extern "C" dfa_status dfa_attn_bwd_ex(const dfa_attn_desc *d, const dfa_block *b
     if (!ptr_aligned(p)) return DFA_E_ALIGN;
   st = check_blocks(d, blocks, n_blocks);
   if (st != DFA_OK) return st;
-  if (d->dtype == DFA_BF16) {
-    // the gradient kernels address 64 streamed rows with 32-bit offsets
-    const int64_t row_bytes = 2 * std::max(std::max(d->q_strides[1], d->o_strides[1]),
-                                           std::max(d->k_strides[1], d->v_strides[1]));
-    for (int64_t i = 0; i < n_blocks; ++i)
-      if (row_bytes * dfa::piece_row_step(blocks[i].stride, blocks[i].run) >= (int64_t{1} << 31) / 64)
-        return DFA_E_UNSUPPORTED;
-  }
+  // the dQ kernel streams K and V, the dK/dV kernel Q and dO (strides of o)
+  st = check_tile_span(d, blocks, n_blocks,
+                       {d->q_strides[1], d->o_strides[1], d->k_strides[1], d->v_strides[1]});
+  if (st != DFA_OK) return st;
   QPlan qp;
   KvPlan kp;
   st = plan_q(d, blocks, n_blocks, dq_tile(d), qp);

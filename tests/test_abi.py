@@ -152,6 +152,45 @@ def test_calls_reject_bad_arguments_before_launch(bd):
     wide.q_strides[:] = [1 << 26, (1 << 24) - 8, 128]
     assert L.dfa_attn_bwd(ctypes.byref(wide), arr, len(blocks), fake, fake, fake, fake, fake, fake,
                           fake, fake, fake, nul, 0, nul) == bd.DFA_E_WORKSPACE
+    # the bf16 forward streams 64 key and value rows with the same 32-bit
+    # offsets: a key (or value) token stride of 2^24 elements is refused by
+    # both modes and by the single-block call, before the workspace check
+    blk0 = bd.DfaBlock(*[int(x) for x in blocks[0]])
+    for name in ("k_strides", "v_strides"):
+        wide = desc(bd)
+        getattr(wide, name)[:] = [1 << 26, 1 << 24, 128]
+        for mode in (bd.DFA_FWD_FUSED, bd.DFA_FWD_STEPWISE):
+            assert L.dfa_attn_fwd(ctypes.byref(wide), arr, len(blocks), mode, fake, fake, fake, fake,
+                                  fake, nul, 0, nul) == bd.DFA_E_UNSUPPORTED, (name, mode)
+        assert L.dfa_attn_block_fwd(ctypes.byref(wide), ctypes.byref(blk0), fake, fake, fake, fake,
+                                    fake, nul) == bd.DFA_E_UNSUPPORTED, name
+        assert L.dfa_attn_bwd(ctypes.byref(wide), arr, len(blocks), fake, fake, fake, fake, fake,
+                              fake, fake, fake, fake, nul, 0, nul) == bd.DFA_E_UNSUPPORTED, name
+        getattr(wide, name)[:] = [1 << 26, (1 << 24) - 8, 128]
+        assert L.dfa_attn_fwd(ctypes.byref(wide), arr, len(blocks), 0, fake, fake, fake, fake,
+                              fake, nul, 0, nul) == bd.DFA_E_WORKSPACE, name
+    # the row step of a token-striped piece multiplies the token stride
+    striped = np.ascontiguousarray(bd.dfa_schedule_build(bd.DFA_SCHED_STRIPED, 256, 4))
+    wide = desc(bd)
+    wide.k_strides[:] = [1 << 26, 1 << 22, 128]  # 64 rows x 4 positions x 2^22 x 2 bytes = 2^31
+    assert L.dfa_attn_fwd(ctypes.byref(wide), striped.ctypes.data_as(ctypes.c_void_p), len(striped),
+                          0, fake, fake, fake, fake, fake, nul, 0, nul) == bd.DFA_E_UNSUPPORTED
+    assert L.dfa_attn_fwd(ctypes.byref(wide), arr, len(blocks), 0, fake, fake, fake, fake, fake,
+                          nul, 0, nul) == bd.DFA_E_WORKSPACE  # contiguous pieces: row step 1
+    # fp32 kernels address rows with 64-bit positions: no such limit
+    wide = desc(bd, dtype=bd.DFA_F32)
+    wide.k_strides[:] = [1 << 26, 1 << 24, 128]
+    assert L.dfa_attn_fwd(ctypes.byref(wide), arr, len(blocks), 0, fake, fake, fake, fake, fake,
+                          nul, 0, nul) == bd.DFA_E_WORKSPACE
+    # the softmax scale must be finite and positive (each row's reference is
+    # its largest scaled score)
+    for bad_scale in (0.0, -0.088, float("inf"), float("nan")):
+        assert ws_size(bd, desc(bd, softmax_scale=bad_scale), blocks, 0)[0] == bd.DFA_E_SHAPE
+        assert L.dfa_attn_fwd(ctypes.byref(desc(bd, softmax_scale=bad_scale)), arr, len(blocks), 0,
+                              fake, fake, fake, fake, fake, nul, 0, nul) == bd.DFA_E_SHAPE
+        assert L.dfa_attn_bwd(ctypes.byref(desc(bd, softmax_scale=bad_scale)), arr, len(blocks),
+                              fake, fake, fake, fake, fake, fake, fake, fake, fake, nul, 0,
+                              nul) == bd.DFA_E_SHAPE
     # runs: a multiple of 64 (row tiles), whole runs, runs that do not overlap
     sb = bd.dfa_schedule_build_striped_blocks(256, 2, 64)
     sarr = np.ascontiguousarray(sb)
