@@ -77,32 +77,6 @@ def schedule(dfa, wl):
     return dfa.dfa_schedule_build(wl["kind"], wl["N"], wl["P"])
 
 
-class HipEvents:
-    """Minimal HIP event timing through libamdhip64 (events on a given stream)."""
-
-    def __init__(self):
-        self.h = ctypes.CDLL("libamdhip64.so")
-        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        self.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
-                                               ctypes.c_void_p]
-        self.h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
-        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
-
-    def create(self):
-        e = ctypes.c_void_p()
-        if self.h.hipEventCreate(ctypes.byref(e)) != 0:
-            raise RuntimeError("hipEventCreate failed")
-        return e
-
-    def elapsed(self, a, b) -> float:
-        self.h.hipEventSynchronize(b)
-        ms = ctypes.c_float()
-        if self.h.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
-            raise RuntimeError("hipEventElapsedTime failed")
-        return float(ms.value)
-
-
 def source_hash(kernel_file: str) -> str:
     """sha256[:16] over a kernel source file and every header in csrc/ (the
     kernels include all of them), so any change to the code that builds the
@@ -236,6 +210,7 @@ def main() -> int:
                        device=dev)
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
+    from long_context_sequence_dfa_amd.timeline import HipEvents
     ev = HipEvents()
     # per step: fwd begin, fwd end, then the backward's marks
     ev_all = [[ev.create() for _ in range(9)] for _ in range(args.steps)]
@@ -299,10 +274,11 @@ def main() -> int:
     alt_ms = ev.elapsed(e0, e1) / n_alt
     del ws_alt, o_alt, lse_alt
 
-    # measured per-(rank, step) slot times of the forward: the idle bubble a
-    # synchronous ring of P devices would see with these block costs
+    # measured per-(rank, step) slot times of one ring-faithful stepwise
+    # forward (each slot launched on its own between events): the idle
+    # bubble a synchronous ring of P devices would see with these slot costs
     full = schedule(dfa, wl)  # every rank, also for a rank's share
-    slot_ms = timeline.rank_step_times(tq, tk, tv, full, wl["P"], repeats=3, stream=stream, docs=td)
+    slot_ms = timeline.slot_times(tq, tk, tv, full, wl["P"], stream=stream, docs=td)
     bubble_measured = timeline.measured_balance(slot_ms)["bubble"]
 
     per = {name: float(np.mean([ev.elapsed(m[a], m[b]) for m in ev_all]))

@@ -322,6 +322,36 @@ dfa_status dfa_attn_bwd_ex(const dfa_attn_desc *d, const dfa_block *blocks, int6
                            void *stream);
 
 /*
+ * Timing marks of a ring-faithful forward, one per (rank, step) slot.
+ * events is a host array of n_ranks * n_ranks + 1 hipEvent_t handles (as
+ * void*) created by the caller.
+ */
+typedef struct dfa_slot_marks {
+  void **events;
+  int32_t n_ranks;
+} dfa_slot_marks;
+
+/*
+ * dfa_attn_fwd_slots -- the stepwise forward (DFA_FWD_STEPWISE semantics
+ * and results) launched one (rank, step) slot at a time, as P devices of a
+ * synchronous ring would run it: the slots go out in (step, rank) order,
+ * events[s * P + r] is recorded on the stream right before slot (r, s) --
+ * also for a slot without blocks -- and events[P * P] after the last, so
+ * the elapsed time between consecutive events is one slot's time on the
+ * GPU (the per-rank timeline behind the idle-bubble figures of the
+ * DistFlashAttn Guide, "Breakdown of Idle Time and Bubble Elimination", and
+ * the Striped Attention Guide, "End-to-End Throughput Scaling").  Blocks must have rank and step
+ * in [0, n_ranks) (else DFA_E_SHAPE); marks and marks->events must not be
+ * NULL; n_ranks >= 1.  Workspace: dfa_workspace_size(DFA_OP_FWD_STEPWISE).
+ * An event that fails to record returns DFA_E_HIP after the work is
+ * enqueued.
+ */
+dfa_status dfa_attn_fwd_slots(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n_blocks,
+                              const void *q, const void *k, const void *v, void *o, float *lse,
+                              void *workspace, size_t ws_bytes, const dfa_slot_marks *marks,
+                              void *stream);
+
+/*
  * dfa_workspace_size -- bytes of workspace `op` (DFA_OP_*) needs for this
  * descriptor and block list.  Pure host computation.
  */

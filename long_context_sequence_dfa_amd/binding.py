@@ -26,7 +26,8 @@ DFA_OP_FWD_FUSED, DFA_OP_FWD_STEPWISE, DFA_OP_BWD = 0, 1, 2
 
 EXPORTED = ("dfa_schedule_build", "dfa_schedule_build_striped_blocks", "dfa_schedule_balance",
             "dfa_attn_block_fwd", "dfa_lse_merge",
-            "dfa_attn_fwd", "dfa_attn_bwd", "dfa_attn_bwd_ex", "dfa_workspace_size",
+            "dfa_attn_fwd", "dfa_attn_fwd_slots", "dfa_attn_bwd", "dfa_attn_bwd_ex",
+            "dfa_workspace_size",
             "dfa_rope", "dfa_status_string")
 BLOCK_FIELDS = ("rank", "step", "kv_rank", "q_start", "kv_start", "len_q", "len_kv", "stride",
                 "diag_offset", "pairs", "run")
@@ -58,6 +59,10 @@ class DfaKernelMarks(ctypes.Structure):
                 ("end", ctypes.c_void_p)]
 
 
+class DfaSlotMarks(ctypes.Structure):
+    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)), ("n_ranks", ctypes.c_int32)]
+
+
 class DfaError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -84,6 +89,7 @@ def lib() -> ctypes.CDLL:
             L.dfa_attn_block_fwd.argtypes = [p, p, p, p, p, p, p, p]
             L.dfa_lse_merge.argtypes = [i64, i32, p, p, p, p, p]
             L.dfa_attn_fwd.argtypes = [p, p, i64, i32, p, p, p, p, p, p, sz, p]
+            L.dfa_attn_fwd_slots.argtypes = [p, p, i64, p, p, p, p, p, p, sz, p, p]
             L.dfa_attn_bwd.argtypes = [p, p, i64, p, p, p, p, p, p, p, p, p, p, sz, p]
             L.dfa_attn_bwd_ex.argtypes = [p, p, i64, p, p, p, p, p, p, p, p, p, p, sz, p, p]
             L.dfa_workspace_size.argtypes = [p, p, i64, i32, ctypes.POINTER(sz)]
@@ -296,6 +302,33 @@ def dfa_attn_fwd(q, k, v, blocks, mode=DFA_FWD_FUSED, o=None, lse=None, workspac
     return o, lse
 
 
+def dfa_attn_fwd_slots(q, k, v, blocks, events, n_ranks, o=None, lse=None, workspace=None,
+                       scale=None, stream=None, docs=None):
+    """The stepwise forward launched one (rank, step) slot at a time in (step,
+    rank) order; ``events`` holds n_ranks^2 + 1 hipEvent_t handles (ints or
+    c_void_p): events[s * n_ranks + r] is recorded before slot (r, s) and the
+    last one at the end.  Returns (o, lse)."""
+    import torch
+    B, N, Hq, D = q.shape
+    if len(events) != n_ranks * n_ranks + 1:
+        raise ValueError("need n_ranks^2 + 1 events")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    desc = make_desc(q, k, v, o, scale, docs)
+    arr = _blocks_arg(blocks)
+    ws, nbytes = _workspace(desc, arr, DFA_OP_FWD_STEPWISE, q.device, workspace)
+    ev = (ctypes.c_void_p * len(events))(*[e.value if isinstance(e, ctypes.c_void_p) else e
+                                           for e in events])
+    marks = DfaSlotMarks(ctypes.cast(ev, ctypes.POINTER(ctypes.c_void_p)), int(n_ranks))
+    _check(lib().dfa_attn_fwd_slots(ctypes.byref(desc), arr.ctypes.data_as(ctypes.c_void_p),
+                                    arr.shape[0], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                    _ptr(ws), nbytes, ctypes.byref(marks), _stream(stream)),
+           "dfa_attn_fwd_slots")
+    return o, lse
+
+
 def dfa_attn_bwd(q, k, v, o, d_o, lse, blocks, dq=None, dk=None, dv=None, workspace=None,
                  scale=None, stream=None, marks=None, docs=None):
     """Gradients (dq, dk, dv) of the forward over the same block list.
@@ -319,3 +352,4 @@ def dfa_attn_bwd(q, k, v, o, d_o, lse, blocks, dq=None, dk=None, dv=None, worksp
     else:
         _check(lib().dfa_attn_bwd_ex(*args, ctypes.byref(marks), _stream(stream)), "dfa_attn_bwd_ex")
     return dq, dk, dv
+

@@ -411,6 +411,62 @@ void plan_steps(const dfa_block *blocks, int64_t n, int tileq, StepPlan &sp) {
   }
 }
 
+// Ring-faithful slots: the blocks of one (rank, step) slot in rounds of
+// distinct query pieces, slots in (step, rank) order.  Same tables as
+// plan_steps (one QSeg and KvRef per block), so the same workspace size.
+void plan_slots(const dfa_block *blocks, int64_t n, int tileq, int P, StepPlan &sp,
+                std::vector<int32_t> &round_slot) {
+  std::vector<int64_t> idx(static_cast<size_t>(n));
+  for (int64_t i = 0; i < n; ++i) idx[i] = i;
+  std::stable_sort(idx.begin(), idx.end(), [&](int64_t a, int64_t b) {
+    return std::make_tuple(blocks[a].step, blocks[a].rank, blocks[a].kv_start) <
+           std::make_tuple(blocks[b].step, blocks[b].rank, blocks[b].kv_start);
+  });
+  size_t pos = 0;
+  while (pos < idx.size()) {
+    const dfa_block &b0 = blocks[idx[pos]];
+    size_t end = pos;
+    while (end < idx.size() && blocks[idx[end]].step == b0.step && blocks[idx[end]].rank == b0.rank)
+      ++end;
+    std::vector<std::vector<int64_t>> rounds;
+    std::vector<std::vector<PieceKey>> used;
+    for (size_t p = pos; p < end; ++p) {
+      const dfa_block &b = blocks[idx[p]];
+      PieceKey key{b.q_start, b.len_q, b.stride, b.run};
+      size_t r = 0;
+      while (r < rounds.size() && std::find(used[r].begin(), used[r].end(), key) != used[r].end()) ++r;
+      if (r == rounds.size()) {
+        rounds.emplace_back();
+        used.emplace_back();
+      }
+      rounds[r].push_back(idx[p]);
+      used[r].push_back(key);
+    }
+    for (const auto &rb : rounds) {
+      StepPlan::Round R{static_cast<int32_t>(sp.tiles.size()), 0};
+      for (int64_t bi : rb) {
+        const dfa_block &b = blocks[bi];
+        QSeg s{};
+        s.q_start = b.q_start;
+        s.len_q = b.len_q;
+        s.stride = b.stride;
+        s.run = b.run;
+        s.blk_begin = static_cast<int32_t>(sp.kv.size());
+        s.blk_count = 1;
+        sp.kv.push_back(KvRef{b.kv_start, b.len_kv, b.diag_offset});
+        const int32_t sid = static_cast<int32_t>(sp.segs.size());
+        sp.segs.push_back(s);
+        const int64_t nt = ceil_div(b.len_q, tileq);
+        for (int64_t t = 0; t < nt; ++t) sp.tiles.push_back(Tile{sid, static_cast<int32_t>(t)});
+      }
+      R.tile_count = static_cast<int32_t>(sp.tiles.size()) - R.tile_begin;
+      sp.rounds.push_back(R);
+      round_slot.push_back(static_cast<int32_t>(b0.step * P + b0.rank));
+    }
+    pos = end;
+  }
+}
+
 // Workspace layouts (offsets in bytes).
 struct FusedLayout {
   size_t segs, kv, tiles, total;
@@ -480,6 +536,63 @@ dfa_status check_ws(void *ws, size_t have, size_t need) {
   if (have < need) return DFA_E_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) % kAlign) return DFA_E_ALIGN;
   return DFA_OK;
+}
+
+// Stepwise forward over a planned list of rounds: accumulators set to the
+// merge identity, each round's partials merged into the accumulator rows in
+// the partial kernel's epilogue, then O and LSE written from them.  With
+// events, events[slot] is recorded before the first round of each slot in
+// slot order (empty slots included) and events[n_slots] at the end.
+dfa_status run_stepwise(const dfa_attn_desc *d, const StepPlan &sp, const int32_t *round_slot,
+                        int32_t n_slots, void *const *events, dfa::FwdArgs a, void *o, float *lse,
+                        void *workspace, size_t ws_bytes, hipStream_t s) {
+  const StepLayout L = step_layout(d, sp);
+  dfa_status st = check_ws(workspace, ws_bytes, L.total);
+  if (st != DFA_OK) return st;
+  const int hd = d->head_dim;
+  char *ws = static_cast<char *>(workspace);
+  std::vector<char> host(L.acc_o, 0);
+  put(host, L.segs, sp.segs);
+  put(host, L.kv, sp.kv);
+  put(host, L.tiles, sp.tiles);
+  st = upload(workspace, host, L.acc_o, s);
+  if (st != DFA_OK) return st;
+  float *acc_o = reinterpret_cast<float *>(ws + L.acc_o);
+  float *acc_lse = reinterpret_cast<float *>(ws + L.acc_lse);
+  const int64_t BH = static_cast<int64_t>(d->batch) * d->heads_q;
+  const int64_t rows = BH * d->seqlen;
+  st = hip_status(dfa::launch_acc_init(acc_o, acc_lse, rows, hd, s));
+  if (st != DFA_OK) return st;
+  auto launch = [&](const dfa::FwdArgs &args, int64_t grid) {
+    return d->dtype == DFA_BF16 ? dfa::launch_fwd_bf16(args, hd, grid, s)
+                                : dfa::launch_fwd_f32(args, hd, grid, s);
+  };
+  bool mark_ok = true;
+  auto mark = [&](int32_t slot) {
+    if (hipEventRecord(static_cast<hipEvent_t>(events[slot]), s) != hipSuccess) mark_ok = false;
+  };
+  // per round: every block's partial, merged into its query rows (mode 2)
+  a.o = acc_o;
+  a.lse = acc_lse;
+  a.out_mode = 2;
+  a.segs = reinterpret_cast<const QSeg *>(ws + L.segs);
+  a.kv = reinterpret_cast<const KvRef *>(ws + L.kv);
+  int32_t next_slot = 0;
+  for (size_t r = 0; r < sp.rounds.size(); ++r) {
+    if (events)
+      while (next_slot <= round_slot[r]) mark(next_slot++);
+    const auto &R = sp.rounds[r];
+    a.tiles = reinterpret_cast<const Tile *>(ws + L.tiles) + R.tile_begin;
+    a.n_tiles = R.tile_count;
+    st = hip_status(launch(a, static_cast<int64_t>(R.tile_count) * BH));
+    if (st != DFA_OK) return st;
+  }
+  if (events)
+    while (next_slot <= n_slots) mark(next_slot++);  // empty trailing slots, then the end
+  st = hip_status(dfa::launch_finalize(acc_o, acc_lse, o, d->o_strides, d->dtype, lse, d->batch,
+                                       d->heads_q, d->seqlen, hd, s));
+  if (st != DFA_OK) return st;
+  return mark_ok ? DFA_OK : DFA_E_HIP;
 }
 
 }  // namespace
@@ -671,35 +784,41 @@ extern "C" dfa_status dfa_attn_fwd(const dfa_attn_desc *d, const dfa_block *bloc
   // stepwise
   StepPlan sp;
   plan_steps(blocks, n_blocks, fwd_tile(d), sp);
-  const StepLayout L = step_layout(d, sp);
-  st = check_ws(workspace, ws_bytes, L.total);
+  return run_stepwise(d, sp, nullptr, 0, nullptr, a, o, lse, workspace, ws_bytes, s);
+}
+
+extern "C" dfa_status dfa_attn_fwd_slots(const dfa_attn_desc *d, const dfa_block *blocks,
+                                         int64_t n_blocks, const void *q, const void *k,
+                                         const void *v, void *o, float *lse, void *workspace,
+                                         size_t ws_bytes, const dfa_slot_marks *marks,
+                                         void *stream) {
+  dfa_status st = check_desc(d);
   if (st != DFA_OK) return st;
-  char *ws = static_cast<char *>(workspace);
-  std::vector<char> host(L.acc_o, 0);
-  put(host, L.segs, sp.segs);
-  put(host, L.kv, sp.kv);
-  put(host, L.tiles, sp.tiles);
-  st = upload(workspace, host, L.acc_o, s);
+  if (!q || !k || !v || !o || !lse || !marks || !marks->events) return DFA_E_NULL;
+  if (!ptr_aligned(q) || !ptr_aligned(k) || !ptr_aligned(v) || !ptr_aligned(o)) return DFA_E_ALIGN;
+  const int32_t P = marks->n_ranks;
+  if (P < 1 || P > 46340) return DFA_E_SHAPE;  // P * P + 1 events fit an int32
+  st = check_blocks(d, blocks, n_blocks);
   if (st != DFA_OK) return st;
-  float *acc_o = reinterpret_cast<float *>(ws + L.acc_o);
-  float *acc_lse = reinterpret_cast<float *>(ws + L.acc_lse);
-  const int64_t rows = BH * d->seqlen;
-  st = hip_status(dfa::launch_acc_init(acc_o, acc_lse, rows, hd, s));
+  for (int64_t i = 0; i < n_blocks; ++i)
+    if (blocks[i].rank < 0 || blocks[i].rank >= P || blocks[i].step < 0 || blocks[i].step >= P)
+      return DFA_E_SHAPE;
+  st = check_tile_span(d, blocks, n_blocks, {d->k_strides[1], d->v_strides[1]});
   if (st != DFA_OK) return st;
-  // per round: every block's partial, merged into its query rows (mode 2)
-  a.o = acc_o;
-  a.lse = acc_lse;
-  a.out_mode = 2;
-  a.segs = reinterpret_cast<const QSeg *>(ws + L.segs);
-  a.kv = reinterpret_cast<const KvRef *>(ws + L.kv);
-  for (const auto &R : sp.rounds) {
-    a.tiles = reinterpret_cast<const Tile *>(ws + L.tiles) + R.tile_begin;
-    a.n_tiles = R.tile_count;
-    st = hip_status(launch(a, static_cast<int64_t>(R.tile_count) * BH));
-    if (st != DFA_OK) return st;
-  }
-  return hip_status(dfa::launch_finalize(acc_o, acc_lse, o, d->o_strides, d->dtype, lse,
-                                         d->batch, d->heads_q, d->seqlen, hd, s));
+  QPlan qp;  // validates piece disjointness
+  st = plan_q(d, blocks, n_blocks, fwd_tile(d), qp);
+  if (st != DFA_OK) return st;
+  StepPlan sp;
+  std::vector<int32_t> round_slot;
+  plan_slots(blocks, n_blocks, fwd_tile(d), P, sp, round_slot);
+  dfa::FwdArgs a{};
+  a.runs = any_runs(blocks, n_blocks);
+  a.g = make_geom(d);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  return run_stepwise(d, sp, round_slot.data(), P * P, marks->events, a, o, lse, workspace,
+                      ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 extern "C" dfa_status dfa_attn_bwd(const dfa_attn_desc *d, const dfa_block *blocks,

@@ -2,20 +2,89 @@
 
 The pages judge a schedule by how long each rank computes at each ring step:
 a step lasts as long as its slowest rank, and the time the other ranks wait
-is the idle bubble (DistFlashAttn paper record, "Core Innovation 1" and its
-utilisation figure; Striped Attention Guide, "Why Striping Solves Load
-Imbalance").  On one GPU every (rank, step) slot can be timed on its own:
-each block of the slot runs alone through dfa_attn_block_fwd between two
-events on the stream, and the slot's time is the sum over its blocks.  The
-same slot times, combined the way a synchronous ring combines them, give
-the measured counterpart of the pair-count balance that
-dfa_schedule_balance computes from the block list.
+is the idle bubble (DistFlashAttn Guide, "Breakdown of Idle Time and Bubble
+Elimination"; Striped Attention Guide, "Why Striping Solves Load Imbalance"
+and "End-to-End Throughput Scaling").  On one GPU every (rank, step) slot
+can be timed on its own.  slot_times runs one ring-faithful stepwise
+forward (dfa_attn_fwd_slots) whose slots are launched one after the other
+in (step, rank) order between HIP events, so each slot's time is its own
+launches' time on the GPU.  rank_step_times instead times each block alone
+through dfa_attn_block_fwd (median of repeats) and sums a slot's blocks.
+The slot times, combined the way a synchronous ring combines them
+(measured_balance), give the measured counterpart of the pair-count balance
+that dfa_schedule_balance computes from the block list.
 """
 from __future__ import annotations
+
+import ctypes
 
 import numpy as np
 
 from . import binding
+
+
+class HipEvents:
+    """HIP events through libamdhip64 (the runtime torch already loaded)."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        if self.h.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
+    def destroy(self, e) -> None:
+        self.h.hipEventDestroy(e)
+
+    def elapsed(self, a, b) -> float:
+        """Milliseconds from event a to event b (waits for b)."""
+        if self.h.hipEventSynchronize(b) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        ms = ctypes.c_float()
+        if self.h.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+
+def slot_times(q, k, v, blocks, n_ranks: int, stream=None, docs=None, warmup: int = 1):
+    """Milliseconds per (rank, step) slot, shape [n_ranks, n_ranks], from one
+    ring-faithful stepwise forward (after ``warmup`` untimed ones): slot (r, s)
+    is the time between the events recorded right before its launches and
+    right before the next slot's.  Slots without blocks cost only the gap
+    between two event records."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    P = int(n_ranks)
+    hip = HipEvents()
+    ev = [hip.create() for _ in range(P * P + 1)]
+    try:
+        o = torch.empty_like(q)
+        lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+        desc = binding.make_desc(q, k, v, o, docs=docs)
+        ws = torch.empty(max(binding.dfa_workspace_size(desc, blocks, binding.DFA_OP_FWD_STEPWISE), 256),
+                         dtype=torch.uint8, device=q.device)
+        for _ in range(max(warmup, 0) + 1):
+            binding.dfa_attn_fwd_slots(q, k, v, blocks, ev, P, o=o, lse=lse, workspace=ws,
+                                       stream=stream, docs=docs)
+        times = np.zeros((P, P), dtype=np.float64)
+        for s in range(P):
+            for r in range(P):
+                i = s * P + r
+                times[r, s] = hip.elapsed(ev[i], ev[i + 1])
+        return times
+    finally:
+        torch.cuda.synchronize()
+        for e in ev:
+            hip.destroy(e)
 
 
 def rank_step_times(q, k, v, blocks, n_ranks: int, repeats: int = 3, scale=None, stream=None,

@@ -31,26 +31,49 @@ def test_measured_balance_closed_forms():
     assert timeline.measured_balance(np.zeros((3, 3)))["bubble"] == 0.0
 
 
+# RING's measured bubble may differ from the pair-count bubble only through
+# per-slot costs that are not proportional to the pairs: the diagonal
+# block's mask work and tile granularity (a 64-key-tile triangle of C = 4096
+# keys is 51 % of a full block's tiles, not 50 %) and the launch gap of each
+# busy slot (a few per cent of a 0.3 ms full block).  With full blocks of
+# cost F and diagonal blocks of cost T, the ring's bubble is
+# 1 - (T + (P-1) F / 2) / (T + (P-1) F): T/F from 0.45 to 0.65 and a gap up to
+# 10 % of F move it by less than 0.02 from the pair count's 0.467 at P = 8.
+RING_TOL = 0.03
+# Folded and striped slots carry equal pairs; what remains is the same
+# per-slot overhead, e.g. the folded schedule's step-0 slots hold three
+# blocks in two launches where later slots hold two full blocks in one.
+BALANCED_STRIPED_MAX = 0.03
+
+
 @pytest.mark.gpu
-def test_measured_bubbles_of_the_three_schedules():
+def test_measured_bubbles_against_the_computed_ones():
+    """One ring-faithful stepwise forward per schedule at the benchmark's
+    shape (N = 32768, P = 8, 32 heads, d = 128), each (rank, step) slot
+    launched on its own between events; the synchronous-ring accounting of
+    the slot times against the oracle's pair-count bubble of the same
+    schedule."""
     import torch
     from long_context_sequence_dfa_amd import inputs
-    N, P, H, D = 16384, 8, 32, 128
+    from oracle import schedule_ref as sr
+    N, P, H, D = 32768, 8, 32, 128
     q, k, v = inputs.workload_tensors(1003, 1, N, H, H, D, "bf16", 1 / math.sqrt(D))
     tq, tk, tv = (inputs.to_torch(x, "bf16", "cuda") for x in (q, k, v))
+    del q, k, v
     out = {}
-    for kind in (0, 1, 2):
+    for kind in (sr.RING, sr.BALANCED, sr.STRIPED):
         blocks = binding.dfa_schedule_build(kind, N, P)
-        t = timeline.rank_step_times(tq, tk, tv, blocks, P, repeats=2)
+        t = timeline.slot_times(tq, tk, tv, blocks, P)
         assert (t >= 0).all() and t.sum() > 0
-        out[kind] = timeline.measured_balance(t)["bubble"]
-        print(f"schedule {kind}: measured bubble {out[kind]:.3f}, computed "
-              f"{binding.dfa_schedule_balance(blocks, P)['bubble']:.3f}", flush=True)
-    # the contiguous ring leaves ranks idle while the diagonal's owner works;
-    # folding and striping spread the causal triangle evenly
-    assert out[0] > 0.3
-    assert out[1] < 0.2 and out[2] < 0.2
-    assert out[0] > 2 * max(out[1], out[2])
+        measured = timeline.measured_balance(t)["bubble"]
+        computed = sr.balance(sr.enumerate_schedule(kind, N, P), P)["bubble"]
+        out[kind] = (measured, computed)
+        print(f"schedule {sr.KIND_NAMES[kind]}: measured bubble {measured:.4f}, computed {computed:.4f}, "
+              f"slot ms min/max of busy slots {t[t > 0.02].min():.3f}/{t.max():.3f}", flush=True)
+    m_ring, c_ring = out[sr.RING]
+    assert abs(m_ring - c_ring) <= RING_TOL
+    for kind in (sr.BALANCED, sr.STRIPED):
+        assert out[kind][0] <= BALANCED_STRIPED_MAX, (sr.KIND_NAMES[kind], out[kind])
 
 
 @pytest.mark.parametrize("kind,N,P,stripe", [(0, 64, 4, 1), (1, 96, 3, 1), (2, 64, 8, 1), (3, 128, 2, 8)])
