@@ -65,9 +65,9 @@ def test_ring_fp32_blocks_merge_and_full(dfa):
         check_out(bhnd(to_np(o)), ro, to_np(lse), rl, "f32", f"fwd mode {mode}")
     dq, dk, dv = dfa.dfa_attn_bwd(tq, tk, tv, o, tdo, lse, blocks)
     torch.cuda.synchronize()
-    rdq, rdk, rdv = oracle.attn_grads(q, k, v, do, scale)
-    for n, g, r in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
-        check_grad(bhnd(to_np(g)), r, None, "f32", n)
+    (rdq, rdk, rdv), (adq, adk, adv) = oracle.attn_grads(q, k, v, do, scale, with_abs=True)
+    for n, g, r, a in (("dq", dq, rdq, adq), ("dk", dk, rdk, adk), ("dv", dv, rdv, adv)):
+        check_grad(bhnd(to_np(g)), r, a, "f32", n, n_terms=N)
 
 
 # ------------------------------------------------------------ bf16 matrix
@@ -96,7 +96,7 @@ def with_dtypes(cases, f32_ok):
     return out
 
 
-@pytest.mark.parametrize("case,dtype", with_dtypes(CASES, lambda c: c[1] <= 1024 and c[4] <= 2))
+@pytest.mark.parametrize("case,dtype", with_dtypes(CASES, lambda c: True))
 def test_forward_backward_parity(dfa, case, dtype):
     kind, N, P, B, Hq, Hkv, D, sub = case
     say(f"case: {sr.KIND_NAMES[kind]} N={N} P={P} B={B} Hq={Hq} Hkv={Hkv} D={D} rank={sub} {dtype}")
@@ -117,9 +117,7 @@ STRIPE_CASES = [
 ]
 
 
-# fp32 sums over > 1K keys drift past 1e-4 rms(g) in summation order, so the
-# fp32 path runs the smaller stripe cases only
-@pytest.mark.parametrize("case,dtype", with_dtypes(STRIPE_CASES, lambda c: c[0] <= 1280 and c[4] <= 2))
+@pytest.mark.parametrize("case,dtype", with_dtypes(STRIPE_CASES, lambda c: True))
 def test_stripe_block_parity(dfa, case, dtype):
     N, P, stripe, B, Hq, Hkv, D, sub = case
     say(f"case: stripe blocks N={N} P={P} stripe={stripe} B={B} Hq={Hq} Hkv={Hkv} D={D} "
@@ -170,9 +168,12 @@ def check_schedule(dfa, blocks, seed, N, B, Hq, Hkv, D, dtype, docs=None, arrays
     (rdq, rdk, rdv), (adq, adk, adv) = oracle.attn_grads(q, k, v, do, scale, rows=rows, with_abs=True,
                                                           docs=docs)
     gq, gk, gv = bhnd(to_np(dq)), bhnd(to_np(dk)), bhnd(to_np(dv))
-    check_grad(gq[:, :, rows], rdq, adq, dtype, "dq", check_mean=grad_mean)
-    check_grad(gk[:, :, krows], rdk[:, :, krows], adk[:, :, krows], dtype, "dk", check_mean=grad_mean)
-    check_grad(gv[:, :, krows], rdv[:, :, krows], adv[:, :, krows], dtype, "dv", check_mean=grad_mean)
+    nq, nk = N, N * (Hq // Hkv)  # terms per dQ element, per dK/dV element (at most)
+    check_grad(gq[:, :, rows], rdq, adq, dtype, "dq", check_mean=grad_mean, n_terms=nq)
+    check_grad(gk[:, :, krows], rdk[:, :, krows], adk[:, :, krows], dtype, "dk", check_mean=grad_mean,
+               n_terms=nk)
+    check_grad(gv[:, :, krows], rdv[:, :, krows], adv[:, :, krows], dtype, "dv", check_mean=grad_mean,
+               n_terms=nk)
     # rows no block touches are zero, including key rows of other ranks
     for g, touched in ((gq, rows), (gk, krows), (gv, krows)):
         assert np.all(g[:, :, np.setdiff1d(np.arange(N), touched)] == 0)
@@ -192,7 +193,7 @@ DOC_CASES = [
 ]
 
 
-@pytest.mark.parametrize("case,dtype", with_dtypes(DOC_CASES, lambda c: c[1] <= 1024 and c[5] <= 2))
+@pytest.mark.parametrize("case,dtype", with_dtypes(DOC_CASES, lambda c: True))
 def test_document_mask_parity(dfa, case, dtype):
     from long_context_sequence_dfa_amd import inputs
     kind, N, P, stripe, B, Hq, Hkv, D, sub, (lmin, lmax) = case
@@ -263,8 +264,10 @@ def test_merge_kernel_against_oracle(dfa):
 # bounds.  For the bf16 gradients only the elementwise bound applies: the
 # large shared components cancel exactly in dQ = scale sum_j dS_ij k_j (the
 # dS of a row sum to zero) and in dK, so the true gradients are small
-# against their terms, and a mean error measured against their rms says
-# nothing about the kernels; the elementwise bound scales with the terms.
+# against their terms; a float64 emulation of the kernels' bf16 roundings
+# alone misses the mean bound by 100x on these inputs (dQ mean error 0.2
+# rms, tests/test_tolerance.py), while the elementwise bound scales with the
+# terms and holds.
 # bf16 only: the fp32 path's gradient bound is relative to rms alone, which
 # the same cancellation puts out of reach of any fp32 summation.
 @pytest.mark.parametrize("dtype", ["bf16"])
@@ -307,8 +310,10 @@ def test_empty_block_list_and_tiny_sequences(dfa):
         ro, rl = oracle.attn_rows(q, k, v, scale)
         check_out(bhnd(to_np(o)), ro, to_np(lse), rl, "bf16", f"tiny {kind} {N} {P}")
         (rdq, rdk, rdv), (a1, a2, a3) = oracle.attn_grads(q, k, v, do, scale, with_abs=True)
-        # a mean over a few hundred cancelling elements is not a statistic;
-        # the elementwise bound still applies
+        # the elementwise bound only: on 1-8 tokens the mean error over a few
+        # hundred elements follows which roundings happen -- an emulation of
+        # the kernels' roundings puts it on both sides of 2e-3 rms depending
+        # on the (equally exact) softmax reference (tests/test_tolerance.py)
         check_grad(bhnd(to_np(dq)), rdq, a1, "bf16", "dq", check_mean=False)
         check_grad(bhnd(to_np(dk)), rdk, a2, "bf16", "dk", check_mean=False)
         check_grad(bhnd(to_np(dv)), rdv, a3, "bf16", "dv", check_mean=False)

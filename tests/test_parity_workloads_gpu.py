@@ -1,9 +1,15 @@
-"""GPU parity at the full workload sizes, on sampled outputs the fp64 oracle
-computes one by one: output rows and LSE of sampled query rows (random,
-first, last, chunk edges), dQ of those rows, and dK/dV of the last key rows
-(whose query rows the oracle can afford).  Heads are sampled as whole
-grouped-query groups so the oracle sees a consistent sub-problem.  The launch
-configuration is the benchmark's (fused forward, the same block lists)."""
+"""GPU parity at the full workload sizes, on outputs the fp64 oracle computes
+one by one: output rows and LSE of sampled query rows (random, first, last,
+chunk edges), dQ of those rows, and dK/dV of the last key rows (whose query
+rows the oracle can afford); for the benchmark's workload (and the
+grouped-query schedule at a length the oracle affords) every dQ row of one
+head and the first 64 keys of every chunk -- the keys read by the most
+query pieces, the key-major kernel's longest walks -- against every query
+row that sees them.  Heads are sampled as whole grouped-query groups so the
+oracle sees a consistent sub-problem.  Whole-tensor invariants (sum_j dK_j =
+0, sum_j dV_j = sum_i dO_i) cover every head, with bounds computed from the
+inputs alone.  The launch configuration is the benchmark's (fused forward,
+the same block lists)."""
 import math
 
 import numpy as np
@@ -12,7 +18,7 @@ import torch
 
 import oracle
 from oracle import schedule_ref as sr
-from tests.parity_util import bhnd, check_grad, check_out, rows_of, to_np
+from tests.parity_util import bhnd, check_grad, check_out, rows_of, sum_invariant_bounds, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -89,7 +95,7 @@ def test_workload_sampled_parity(dfa, name):
                                                      docs=docs)
         gq = bhnd(to_np(dq[:, rows][:, :, heads]))
         # the rms of a sampled gradient set stands in for the tensor's
-        check_grad(gq, rdq, adq, "bf16", f"{name} dQ", check_mean=False)
+        check_grad(gq, rdq, adq, "bf16", f"{name} dQ")
         # last key rows: their query rows are the tail of the row set
         tail_rows = rows_all[rows_all >= N - 96]
         keys = np.arange(N - 64, N)
@@ -99,16 +105,77 @@ def test_workload_sampled_parity(dfa, name):
                                               aa=a2, docs=docs)
         gk = bhnd(to_np(dk[:, keys][:, :, [hk]]))
         gv = bhnd(to_np(dv[:, keys][:, :, [hk]]))
-        check_grad(gk, rdk, adk, "bf16", f"{name} dK", check_mean=False)
-        check_grad(gv, rdv, adv, "bf16", f"{name} dV", check_mean=False)
-    # whole-tensor invariants, valid at any size: softmax is shift invariant in
-    # k (sum_j dK_j = 0); sum_j dV_j = sum of dO over the rows and group heads
-    dkf = dk.double()
-    imb = dkf.sum(dim=1).abs()
-    assert torch.all(imb <= 2.0 ** -5 * dkf.abs().sum(dim=1) + 1e-3), f"{name} sum dK"
-    dof = tdo.double()[:, torch.as_tensor(rows_all, device=dev)]
-    want = dof.sum(dim=1).reshape(1, Hkv, group, D).sum(dim=2)
-    got = dv.double().sum(dim=1)
-    assert torch.all((got - want).abs() <= 2.0 ** -5 * dv.double().abs().sum(dim=1) + 1e-3), \
-        f"{name} sum dV"
+        check_grad(gk, rdk, adk, "bf16", f"{name} dK")
+        check_grad(gv, rdv, adv, "bf16", f"{name} dV")
+    check_sum_invariants(name, q, k, v, do, scale, rows_all, dk, dv)
     print(f"case: {name} done", flush=True)
+
+
+def check_sum_invariants(name, q, k, v, do, scale, rows, dk, dv):
+    """Whole-tensor invariants, valid at any size: softmax is shift invariant
+    in k (sum_j dK_j = 0), and sum_j dV_j is the sum of dO over the rows and
+    the group's heads; bounds from the inputs alone (sum_invariant_bounds:
+    2^-8 times the summed error magnitudes, no GPU value in them)."""
+    B, N, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if len(rows) == N:  # every row: no copies of the full tensors
+        rows = slice(None)
+    bk, bv = sum_invariant_bounds(q, k, v, do, scale, rows=None if isinstance(rows, slice) else rows)
+    sk = dk.double().sum(dim=1).cpu().numpy()                 # [B, Hkv, D]
+    sv = dv.double().sum(dim=1).cpu().numpy()
+    want = np.zeros((B, Hkv, D))
+    for h in range(Hq):
+        want[:, h // (Hq // Hkv)] += np.asarray(do[:, rows, h], np.float64).sum(axis=1)
+    rk, rv = float((np.abs(sk) / bk).max()), float((np.abs(sv - want) / bv).max())
+    print(f"case: {name} sum dK error / bound {rk:.4f}, sum dV error / bound {rv:.4f}", flush=True)
+    assert rk <= 1.0, f"{name} sum dK"
+    assert rv <= 1.0, f"{name} sum dV"
+
+
+# the benchmark's workload at full length, and the grouped-query folded
+# schedule at a length whose every query row the oracle affords (P = 32,
+# 64 chunks of 256, so the first chunk's keys are read by 64 query pieces):
+# name, N, Hq, Hkv, P, seed, scaled, kv head checked
+HEAVY = [
+    ("llama7b-n32k-balanced-p8", 32768, 32, 32, 8, 1003, True, 0),
+    ("gqa-32-8-n16k-balanced-p32", 16384, 32, 8, 32, 1005, False, 1),
+]
+
+
+@pytest.mark.parametrize("case", HEAVY, ids=[c[0] for c in HEAVY])
+def test_heavy_keys_full_length(dfa, case):
+    """dK and dV of the first 64 keys of every chunk of the folded schedule
+    (each read by every later query piece: the longest key-major walks,
+    many query tiles summed in the kernel's cost-sorted order, the group's
+    query heads summed for grouped-query attention) against every query row
+    that sees them; and every dQ row of the group's heads.  Mean and
+    elementwise bounds."""
+    from long_context_sequence_dfa_amd import inputs
+    name, N, Hq, Hkv, P, seed, scaled, hk = case
+    D, group = 128, Hq // Hkv
+    print(f"case: heavy keys {name} generating inputs", flush=True)
+    scale = 1 / math.sqrt(D)
+    q, k, v, do = inputs.workload_tensors(seed, 1, N, Hq, Hkv, D, "bf16", scale if scaled else None,
+                                          with_do=True)
+    dev = torch.device("cuda:0")
+    tq, tk, tv, tdo = (inputs.to_torch(x, "bf16", dev) for x in (q, k, v, do))
+    blocks = dfa.dfa_schedule_build(sr.BALANCED, N, P)
+    print(f"case: heavy keys {name} forward + backward on the GPU", flush=True)
+    o, lse = dfa.dfa_attn_fwd(tq, tk, tv, blocks)
+    dq, dk, dv = dfa.dfa_attn_bwd(tq, tk, tv, o, tdo, lse, blocks)
+    torch.cuda.synchronize()
+    heads = list(range(hk * group, (hk + 1) * group))
+    qh, doh = q[:, :, heads], do[:, :, heads]
+    kh, vh = k[:, :, [hk]], v[:, :, [hk]]
+    C = N // (2 * P)
+    keys = np.concatenate([np.arange(c * C, c * C + 64) for c in range(2 * P)])
+    rows = np.arange(N)
+    print(f"case: heavy keys {name} oracle: {len(heads)} heads x {N} rows", flush=True)
+    lse_r, dd_r, rdq, aa, adq = oracle.grad_rows(qh, kh, vh, doh, scale, rows=rows, with_abs=True)
+    print(f"case: heavy keys {name} oracle: {keys.size} keys", flush=True)
+    rdk, rdv, adk, adv = oracle.grad_cols(qh, kh, vh, doh, scale, rows, lse_r, dd_r, keys=keys, aa=aa)
+    check_grad(bhnd(to_np(dq[:, :, heads])), rdq, adq, "bf16", f"{name} dQ (all rows)")
+    check_grad(bhnd(to_np(dk[:, keys][:, :, [hk]])), rdk, adk, "bf16", f"{name} dK (chunk heads)")
+    check_grad(bhnd(to_np(dv[:, keys][:, :, [hk]])), rdv, adv, "bf16", f"{name} dV (chunk heads)")
+    check_sum_invariants(name, q, k, v, do, scale, rows, dk, dv)
+    print(f"case: heavy keys {name} done", flush=True)
