@@ -352,6 +352,29 @@ dfa_status dfa_attn_fwd_slots(const dfa_attn_desc *d, const dfa_block *blocks, i
                               void *stream);
 
 /*
+ * dfa_attn_bwd_noalloc -- dfa_attn_bwd without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the call allocates
+ * nothing and uses the library's fixed scratch of 80 MiB per GPU instead (a
+ * device array each GPU holds from the first use until the process ends).
+ * Same arguments, results and errors as dfa_attn_bwd, plus:
+ *   - DFA_E_WORKSPACE when the problem needs more than the scratch
+ *     (dfa_workspace_size(DFA_OP_BWD) > 80 MiB; about 8 bytes per
+ *     batch x heads_q x seqlen row plus the planning tables), checked on the
+ *     host before anything is enqueued;
+ *   - DFA_E_UNSUPPORTED when `stream` belongs to another device than the
+ *     current one (the scratch used is the current device's).
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in time
+ * on one GPU (other streams, other host threads) race and must be ordered by
+ * the caller.  Nothing in the scratch has to start at zero; each call
+ * rewrites what it reads.
+ */
+dfa_status dfa_attn_bwd_noalloc(const dfa_attn_desc *d, const dfa_block *blocks, int64_t n_blocks,
+                                const void *q, const void *k, const void *v, const void *o,
+                                const void *d_o, const float *lse, void *dq, void *dk, void *dv,
+                                void *stream);
+
+/*
  * dfa_workspace_size -- bytes of workspace `op` (DFA_OP_*) needs for this
  * descriptor and block list.  Pure host computation.
  */

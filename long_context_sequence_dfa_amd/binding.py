@@ -27,7 +27,7 @@ DFA_OP_FWD_FUSED, DFA_OP_FWD_STEPWISE, DFA_OP_BWD = 0, 1, 2
 EXPORTED = ("dfa_schedule_build", "dfa_schedule_build_striped_blocks", "dfa_schedule_balance",
             "dfa_attn_block_fwd", "dfa_lse_merge",
             "dfa_attn_fwd", "dfa_attn_fwd_slots", "dfa_attn_bwd", "dfa_attn_bwd_ex",
-            "dfa_workspace_size",
+            "dfa_attn_bwd_noalloc", "dfa_workspace_size",
             "dfa_rope", "dfa_status_string")
 BLOCK_FIELDS = ("rank", "step", "kv_rank", "q_start", "kv_start", "len_q", "len_kv", "stride",
                 "diag_offset", "pairs", "run")
@@ -92,6 +92,7 @@ def lib() -> ctypes.CDLL:
             L.dfa_attn_fwd_slots.argtypes = [p, p, i64, p, p, p, p, p, p, sz, p, p]
             L.dfa_attn_bwd.argtypes = [p, p, i64, p, p, p, p, p, p, p, p, p, p, sz, p]
             L.dfa_attn_bwd_ex.argtypes = [p, p, i64, p, p, p, p, p, p, p, p, p, p, sz, p, p]
+            L.dfa_attn_bwd_noalloc.argtypes = [p, p, i64, p, p, p, p, p, p, p, p, p, p]
             L.dfa_workspace_size.argtypes = [p, p, i64, i32, ctypes.POINTER(sz)]
             L.dfa_rope.argtypes = [i32, i32, i64, i32, i32, p, p, p, p, i64, ctypes.c_double, i32, p]
             L.dfa_status_string.argtypes = [i32]
@@ -353,3 +354,19 @@ def dfa_attn_bwd(q, k, v, o, d_o, lse, blocks, dq=None, dk=None, dv=None, worksp
         _check(lib().dfa_attn_bwd_ex(*args, ctypes.byref(marks), _stream(stream)), "dfa_attn_bwd_ex")
     return dq, dk, dv
 
+
+def dfa_attn_bwd_noalloc(q, k, v, o, d_o, lse, blocks, dq, dk, dv, scale=None, stream=None,
+                         docs=None):
+    """dfa_attn_bwd without a workspace: the library's fixed per-GPU scratch
+    is used and nothing is allocated (the caller passes dq, dk, dv)."""
+    if d_o.stride() != o.stride():
+        raise ValueError("d_o must have o's strides")
+    if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
+        raise ValueError("gradients must have their primal's strides")
+    desc = make_desc(q, k, v, o, scale, docs)
+    arr = _blocks_arg(blocks)
+    _check(lib().dfa_attn_bwd_noalloc(ctypes.byref(desc), arr.ctypes.data_as(ctypes.c_void_p),
+                                      arr.shape[0], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o),
+                                      _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)),
+           "dfa_attn_bwd_noalloc")
+    return dq, dk, dv
