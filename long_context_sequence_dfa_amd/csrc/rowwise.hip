@@ -89,43 +89,57 @@ __global__ __launch_bounds__(NT) void zero_rows_kernel(char *x, int64_t s0, int6
 }
 
 // -D[b][h][pos] = -sum_c dO[b][pos][h][c] * O[b][pos][h][c] (stored negated: the
-// gradient kernels start their dP accumulators from it) and LSE*log2(e): one
-// thread per row
+// gradient kernels start their dP accumulators from it) and LSE*log2(e).
+// A row is read by LPR lanes, 16 contiguous bytes each, so every load of a
+// wave covers RPW whole rows; each lane keeps U rows' loads in flight, then
+// the row's partial sums meet in a butterfly over its LPR lanes.
 template <int HD, bool BF16>
 __global__ __launch_bounds__(NT) void bwd_pre_kernel(BwdArgs a) {
+  constexpr int EPL = BF16 ? 8 : 4;  // elements per 16-byte load
+  constexpr int LPR = HD / EPL;      // lanes per row
+  constexpr int RPW = 64 / LPR;      // rows per wave and load
+  constexpr int U = 4;               // rows per lane
+  static_assert(HD % EPL == 0 && 64 % LPR == 0, "a row is a whole number of lanes");
   const Geom &G = a.g;
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x;
+  const int lane = threadIdx.x & 63, sub = lane % LPR, grp = lane / LPR;
   const int64_t rows = static_cast<int64_t>(G.batch) * G.hq * G.seqlen;
-  if (tid >= rows) return;
-  const int64_t bh = tid / G.seqlen, pos = tid % G.seqlen;
-  const int64_t b = bh / G.hq, h = bh % G.hq;
-  const int64_t off = b * G.os[0] + pos * G.os[1] + h * G.os[2];
-  float s = 0.f;
-  if (BF16) {
-    const uint16_t *op = static_cast<const uint16_t *>(a.o) + off;
-    const uint16_t *dp = static_cast<const uint16_t *>(a.dout) + off;
+  const int64_t r0 = ((static_cast<int64_t>(blockIdx.x) * NT + threadIdx.x) >> 6) * (RPW * U);
+  if (r0 >= rows) return;  // wave-uniform
+  const int esz = BF16 ? 2 : 4;
+  const char *ob = static_cast<const char *>(a.o), *db = static_cast<const char *>(a.dout);
+  u32x4 ov[U], dv[U];
 #pragma unroll
-    for (int c = 0; c < HD; c += 8) {
-      const u32x4 ov = ld16(op + c), dv = ld16(dp + c);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s = fmaf(__uint_as_float(ov[e] << 16), __uint_as_float(dv[e] << 16), s);
-        s = fmaf(__uint_as_float(ov[e] & 0xffff0000u), __uint_as_float(dv[e] & 0xffff0000u), s);
-      }
-    }
-  } else {
-    const float *op = static_cast<const float *>(a.o) + off;
-    const float *dp = static_cast<const float *>(a.dout) + off;
-#pragma unroll
-    for (int c = 0; c < HD; c += 4) {
-      const f32x4 ov = *reinterpret_cast<const f32x4 *>(op + c);
-      const f32x4 dv = *reinterpret_cast<const f32x4 *>(dp + c);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s = fmaf(ov[e], dv[e], s);
+  for (int u = 0; u < U; ++u) {
+    const int64_t r = r0 + u * RPW + grp;
+    if (r < rows) {
+      const int64_t bh = r / G.seqlen, pos = r % G.seqlen;
+      const int64_t off = esz * ((bh / G.hq) * G.os[0] + pos * G.os[1] + (bh % G.hq) * G.os[2]) + 16 * sub;
+      ov[u] = ld16(ob + off);
+      dv[u] = ld16(db + off);
+    } else {
+      ov[u] = dv[u] = u32x4{0, 0, 0, 0};
     }
   }
-  a.dd[tid] = -s;
-  a.lse2[tid] = a.lse[tid] * kLog2e;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (BF16) {
+        s = fmaf(__uint_as_float(ov[u][e] << 16), __uint_as_float(dv[u][e] << 16), s);
+        s = fmaf(__uint_as_float(ov[u][e] & 0xffff0000u), __uint_as_float(dv[u][e] & 0xffff0000u), s);
+      } else {
+        s = fmaf(__uint_as_float(ov[u][e]), __uint_as_float(dv[u][e]), s);
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < LPR; m <<= 1) s += __shfl_xor(s, m);
+    const int64_t r = r0 + u * RPW + grp;
+    if (sub == 0 && r < rows) {
+      a.dd[r] = -s;
+      a.lse2[r] = a.lse[r] * kLog2e;
+    }
+  }
 }
 
 inline unsigned blocks_for(int64_t threads) { return static_cast<unsigned>((threads + NT - 1) / NT); }
@@ -187,7 +201,9 @@ hipError_t launch_zero_rows(void *x, const int64_t strides[3], int dtype, int ba
 hipError_t launch_bwd_pre(const BwdArgs &a, int dtype, int hd, hipStream_t s) {
   const int64_t rows = static_cast<int64_t>(a.g.batch) * a.g.hq * a.g.seqlen;
   if (rows == 0) return hipSuccess;
-  dim3 gr(blocks_for(rows)), bl(NT);
+  // 64 threads per wave, each wave 4 * 64 / (hd / 8 or hd / 4) rows
+  const int64_t rows_per_wave = 4 * 64 / (dtype == 1 ? hd / 8 : hd / 4);
+  dim3 gr(blocks_for((rows + rows_per_wave - 1) / rows_per_wave * 64)), bl(NT);
   const bool bf = dtype == 1;
   if (hd == 128 && bf)
     hipLaunchKernelGGL((bwd_pre_kernel<128, true>), gr, bl, 0, s, a);

@@ -179,3 +179,56 @@ def test_heavy_keys_full_length(dfa, case):
     check_grad(bhnd(to_np(dv[:, keys][:, :, [hk]])), rdv, adv, "bf16", f"{name} dV (chunk heads)")
     check_sum_invariants(name, q, k, v, do, scale, rows, dk, dv)
     print(f"case: heavy keys {name} done", flush=True)
+
+
+# stepwise forward (per-ring-step partials merged in the kernel epilogue) at
+# full size: the forward workload's shape and schedule, the token-striped
+# rank share, and stripe blocks of 64
+STEPWISE = ["llama7b-n32k-balanced-p8", "llama7b-n131k-striped-p16-rank0", "llama7b-n32k-striped64-p8"]
+
+
+@pytest.mark.parametrize("name", STEPWISE)
+def test_stepwise_forward_full_shape(dfa, name):
+    """The stepwise forward at the workload's full size against the oracle on
+    sampled rows (random, first, last, both sides of every chunk edge) of
+    the sampled heads; every row of every head against the fused forward
+    (the same mathematics through another merge order: agreement within the
+    bf16 output bounds)."""
+    from long_context_sequence_dfa_amd import inputs
+    N, Hq, Hkv, kind, P, seed, scaled, rank, kv_heads = WORKLOADS[name]
+    D, group = 128, Hq // Hkv
+    print(f"case: stepwise {name} generating inputs", flush=True)
+    q, k, v = inputs.workload_tensors(seed, 1, N, Hq, Hkv, D, "bf16", 1 / math.sqrt(D) if scaled else None)
+    dev = torch.device("cuda:0")
+    tq, tk, tv = (inputs.to_torch(x, "bf16", dev) for x in (q, k, v))
+    if kind == sr.STRIPED_BLOCK:
+        blocks = dfa.dfa_schedule_build_striped_blocks(N, P, STRIPE[name])
+    else:
+        blocks = dfa.dfa_schedule_build(kind, N, P)
+    if rank is not None:
+        blocks = blocks[blocks[:, 0] == rank]
+    print(f"case: stepwise {name} forward on the GPU ({len(blocks)} blocks)", flush=True)
+    o, lse = dfa.dfa_attn_fwd(tq, tk, tv, blocks, mode=dfa.DFA_FWD_STEPWISE)
+    of, lf = dfa.dfa_attn_fwd(tq, tk, tv, blocks)
+    torch.cuda.synchronize()
+    rows_all = rows_of(blocks)
+    ridx = torch.as_tensor(rows_all, device=dev)
+    eo = (o[:, ridx].float() - of[:, ridx].float()).abs()
+    el = (lse[:, :, ridx] - lf[:, :, ridx]).abs()
+    print(f"case: stepwise {name} vs fused: O max {eo.max().item():.3e} mean {eo.mean().item():.3e}, "
+          f"LSE max {el.max().item():.3e}", flush=True)
+    assert eo.max().item() <= 2e-2 and eo.mean().item() <= 2e-3 and el.max().item() <= 1e-3
+    rng = np.random.default_rng(seed + 7)
+    chunk = {sr.BALANCED: N // (2 * P), sr.STRIPED_BLOCK: STRIPE.get(name, 1)}.get(kind, N // P)
+    edges = [x for c in range(1, N // chunk) for x in (c * chunk - 1, c * chunk)]
+    cand = np.concatenate([rng.choice(rows_all, 48, replace=False), rows_all[:4], rows_all[-4:],
+                           np.array(edges[:8] + edges[-8:], dtype=np.int64)])
+    rows = np.intersect1d(np.unique(cand), rows_all)
+    scale = 1 / math.sqrt(D)
+    for hk in kv_heads:
+        heads = list(range(hk * group, (hk + 1) * group))
+        print(f"case: stepwise {name} oracle, kv head {hk}, {rows.size} rows", flush=True)
+        ro, rl = oracle.attn_rows(q[:, :, heads], k[:, :, [hk]], v[:, :, [hk]], scale, rows=rows)
+        check_out(bhnd(to_np(o[:, rows][:, :, heads])), ro, to_np(lse[:, heads][:, :, rows]), rl, "bf16",
+                  f"stepwise {name} O")
+    print(f"case: stepwise {name} done", flush=True)
