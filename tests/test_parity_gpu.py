@@ -360,3 +360,35 @@ def test_strided_views(dfa):
     check_grad(bhnd(to_np(dq)), rdq, a1, "bf16", "dq")
     check_grad(bhnd(to_np(dk)), rdk, a2, "bf16", "dk")
     check_grad(bhnd(to_np(dv)), rdv, a3, "bf16", "dv")
+
+
+# every head of each full-size workload's head layout and schedule, at a
+# length whose every row the oracle affords (N = 2048): name, kind, P,
+# stripe, Hq, Hkv, inputs scaled by 1/sqrt(d), subset rank
+ALL_HEADS = [
+    ("llama7b-balanced-p8", BAL, 8, 1, 32, 32, True, None),
+    ("llama7b-striped-p16-rank0", STR, 16, 1, 32, 32, False, 0),
+    ("gqa-32-8-balanced-p32", BAL, 32, 1, 32, 8, False, None),   # chunks of 32 rows
+    ("llama7b-striped64-p8", sr.STRIPED_BLOCK, 8, 64, 32, 32, True, None),
+]
+
+
+@pytest.mark.parametrize("case", ALL_HEADS, ids=[c[0] for c in ALL_HEADS])
+def test_all_heads_at_workload_shapes(dfa, case):
+    """Fused and stepwise forward and the backward on all 32 query heads
+    (d = 128, bf16) of a workload's head layout and schedule, every row and
+    key row the blocks touch against the oracle (the full-size tests sample
+    heads and rows)."""
+    from long_context_sequence_dfa_amd import inputs
+    name, kind, P, stripe, Hq, Hkv, scaled, sub = case
+    N, D = 2048, 128
+    say(f"case: all heads {name} N={N}")
+    if kind == sr.STRIPED_BLOCK:
+        blocks = dfa.dfa_schedule_build_striped_blocks(N, P, stripe)
+    else:
+        blocks = dfa.dfa_schedule_build(kind, N, P)
+    if sub is not None:
+        blocks = blocks[blocks[:, 0] == sub]
+    arrays = inputs.workload_tensors(5000 + P, 1, N, Hq, Hkv, D, "bf16", 1 / np.sqrt(D) if scaled else None,
+                                     with_do=True)
+    check_schedule(dfa, blocks, None, N, 1, Hq, Hkv, D, "bf16", arrays=arrays)

@@ -115,7 +115,7 @@ def check_sum_invariants(name, q, k, v, do, scale, rows, dk, dv):
     """Whole-tensor invariants, valid at any size: softmax is shift invariant
     in k (sum_j dK_j = 0), and sum_j dV_j is the sum of dO over the rows and
     the group's heads; bounds from the inputs alone (sum_invariant_bounds:
-    2^-8 times the summed error magnitudes, no GPU value in them)."""
+    2^-7 times the summed error magnitudes, no GPU value in them)."""
     B, N, Hq, D = q.shape
     Hkv = k.shape[2]
     if len(rows) == N:  # every row: no copies of the full tensors

@@ -10,9 +10,12 @@
   gradients) shows:
   - the literal bound max |dg| <= 2e-2 rms(g) fails even for the exact
     gradient merely rounded to bf16 (gradient elements reach 15-100x rms);
-  - the elementwise bound |dg| <= 2e-2 rms(g) + 2^-8 g_abs holds with margin,
+  - the elementwise bound |dg| <= 2e-2 rms(g) + 2^-7 g_abs holds with margin,
     and so does the mean bound mean |dg| <= 2e-3 rms(g), at the parity
     tests' sizes (so the GPU tests keep both there);
+  - 2^-7 and not 2^-8: bf16's unit roundoff is 2^-8, and a token-striped
+    rank share (rank 0 of 16, N = 2048) has a dV element whose two emulated
+    roundings (P into dV, the stored dV) reach 1.27 times 2^-8 g_abs;
   - on 1-8 tokens the mean statistic follows the rounding pattern: with the
     references the online softmax may keep it lands on both sides of the
     bound, so the tiny-sequence GPU test keeps the elementwise bound only;
@@ -30,7 +33,7 @@ from long_context_sequence_dfa_amd import inputs
 from tests.bf16_emulation import dense_grads, dense_magnitudes, round_bf16
 from tests.parity_util import sum_invariant_bounds
 
-G_MEAN, G_MAX, G_REL = 2e-3, 2e-2, 2.0 ** -8
+G_MEAN, G_MAX, G_REL = 2e-3, 2e-2, 2.0 ** -7
 
 
 def rel_err(a, b):
@@ -210,3 +213,34 @@ def test_sum_invariant_bounds_hold_under_emulation():
         rv = float((np.abs(dv.sum(axis=2) - want_v) / bv).max())
         print(f"N={N}: sum dK error / bound {rk:.4f}, sum dV error / bound {rv:.4f}")
         assert rk <= 0.25 and rv <= 0.25
+
+
+def test_unit_roundoff_of_bf16_sets_the_elementwise_bound():
+    """bf16 keeps 8 significant bits: one rounding errs by up to 2^-8
+    relative (checked on the rounding itself), so a gradient element made
+    of rounded terms and stored in bf16 needs 2^-7 g_abs.  Rank 0's share of
+    token striping over 16 ranks (N = 2048, its query rows only, head 31 of
+    the all-heads GPU case) has a dV element whose emulated roundings exceed
+    2^-8 g_abs by 27 % and stay within 2^-7 g_abs."""
+    # just below the midpoint between 1 and the next bf16 value 1 + 2^-7
+    x = np.array([1 + 2.0 ** -8 - 2.0 ** -20])
+    assert round_bf16(x)[0] == 1.0 and abs(round_bf16(x)[0] - x[0]) / x[0] > 0.99 * 2.0 ** -8
+    N, P, H, D = 2048, 16, 32, 128
+    q, k, v, do = inputs.workload_tensors(5000 + P, 1, N, H, H, D, "bf16", None, with_do=True)
+    head = [31]
+    q, k, v = (np.asarray(t[:, :, head], np.float64) for t in (q, k, v))
+    do = np.array(do[:, :, head], np.float64)
+    share = np.zeros(N, bool)
+    share[::P] = True
+    do[:, ~share] = 0.0  # the loss covers rank 0's query rows only
+    scale = 1 / math.sqrt(D)
+    exact = dense_grads(q, k, v, do, scale)
+    emul = dense_grads(q, k, v, do, scale, emulate=True)
+    mags = dense_magnitudes(q, k, v, do, scale)
+    r, a = exact[2], mags[2]
+    rms = math.sqrt(float((r ** 2).mean()))
+    e = np.abs(emul[2] - r)
+    old = float((e / (G_MAX * rms + 2.0 ** -8 * a)).max())
+    new = float((e / (G_MAX * rms + G_REL * a)).max())
+    print(f"rank-0 share dV: emulated error / (2e-2 rms + 2^-8 g_abs) {old:.3f}, with 2^-7: {new:.3f}")
+    assert old > 1.2 and new < 0.7
