@@ -353,10 +353,13 @@ dfa_status dfa_attn_fwd_slots(const dfa_attn_desc *d, const dfa_block *blocks, i
 
 /*
  * dfa_attn_bwd_noalloc -- dfa_attn_bwd without a workspace argument, for
- * callers that cannot allocate device memory (code under HIP graph capture,
- * tight serving loops, harnesses that forbid hipMalloc): the call allocates
- * nothing and uses the library's fixed scratch of 80 MiB per GPU instead (a
- * device array each GPU holds from the first use until the process ends).
+ * callers that cannot allocate device memory (tight serving loops, harnesses
+ * that forbid hipMalloc): the call allocates no device memory and uses the
+ * library's fixed scratch of 80 MiB per GPU instead (a device array each GPU
+ * holds from the first use until the process ends).  Not for HIP graph
+ * capture: like every call here it uploads its planning tables with an
+ * asynchronous host-to-device copy from a host buffer that is released when
+ * the call returns, which a captured graph would replay.
  * Same arguments, results and errors as dfa_attn_bwd, plus:
  *   - DFA_E_WORKSPACE when the problem needs more than the scratch
  *     (dfa_workspace_size(DFA_OP_BWD) > 80 MiB; about 8 bytes per
