@@ -40,8 +40,18 @@ def bhnd(x):
     return x.transpose(0, 2, 1, 3)
 
 
-def check_out(go, ro, gl, rl, dtype, what=""):
-    """go/ro [..., d] outputs, gl/rl LSE with matching leading dims."""
+def check_out(go, ro, gl, rl, dtype, what="", oabs=None, n_keys=None):
+    """go/ro [..., d] outputs, gl/rl LSE with matching leading dims.
+    ``oabs`` (bf16): the output's error magnitudes sum_j P_ij |v_jc| (the
+    oracle's output with |v| for v); then also elementwise
+    |dO| <= (2^-7 + 2^-12 + (n + 2d + 64) 2^-24) oabs, n the key count: one
+    bf16 rounding of every probability entering P.V plus one of the stored
+    output (u = 2^-8 each), the fp32 score error inside the exponent
+    (2^-12 covers d 2^-24 sum_c |q_c k_c| scale log2(e) for scores up to 30
+    log2 units, which normal inputs of these shapes stay below) and the fp32
+    sums -- a relative check that the absolute bounds cannot give when the
+    inputs are scaled by 1/sqrt(d) and the outputs are small.  ``n_keys``: an
+    upper bound of n (the sequence length)."""
     fin = np.isfinite(rl)
     assert np.array_equal(np.isfinite(gl), fin), f"{what}: -inf rows differ"
     assert np.all(gl[~fin] == rl[~fin]), f"{what}: empty-row LSE"
@@ -54,7 +64,22 @@ def check_out(go, ro, gl, rl, dtype, what=""):
         assert eo.max() <= BF16_O_MAX, (what, "O max", eo.max())
         assert eo.mean() <= BF16_O_MEAN, (what, "O mean", eo.mean())
         assert el.max() <= BF16_LSE_MAX, (what, "LSE max", el.max())
+        if oabs is not None:
+            rel = o_bound_ratio(go, ro, oabs, n_keys)
+            rms = float(np.sqrt((ro ** 2).mean()))
+            print(f"{what}: O max|dO|/rms {eo.max() / rms if rms > 0 else 0.0:.4f}, "
+                  f"elementwise bound ratio {rel:.3f}", flush=True)
+            assert rel <= 1.0, (what, "O elementwise bound ratio", rel)
     return float(eo.max()), float(el.max())
+
+
+def o_bound_ratio(go, ro, oabs, n_keys):
+    """max of |go - ro| / ((2^-7 + 2^-12 + (n + 2d + 64) 2^-24) oabs); exact
+    zeros where oabs is 0 (rows that see no key)."""
+    e = np.abs(go - ro)
+    bound = (G_REL + 2.0 ** -12 + (n_keys + 2 * ro.shape[-1] + 64) * F32_U) * oabs
+    assert np.all(e[bound == 0] == 0)
+    return float((e / np.where(bound > 0, bound, np.inf)).max())
 
 
 def check_grad(g, r, rabs, dtype, what="", check_mean=True, n_terms=None):

@@ -131,7 +131,8 @@ def test_stripe_block_parity(dfa, case, dtype):
         op, lp = dfa.dfa_attn_block_fwd(tq, tk, tv, b)
         torch.cuda.synchronize()
         xo, xl = oracle.block_partial(q, k, v, scale, *b[3:8], run=b[10])
-        check_out(to_np(op), xo, to_np(lp), xl, dtype, f"block {b[:3]}")
+        xa, _ = oracle.block_partial(q, k, np.abs(v), scale, *b[3:8], run=b[10])
+        check_out(to_np(op), xo, to_np(lp), xl, dtype, f"block {b[:3]}", oabs=xa, n_keys=N)
     check_schedule(dfa, blocks, 4000 + N + P, N, B, Hq, Hkv, D, dtype)
 
 
@@ -153,12 +154,13 @@ def check_schedule(dfa, blocks, seed, N, B, Hq, Hkv, D, dtype, docs=None, arrays
     td = None if docs is None else torch.tensor(docs, dtype=torch.int32, device="cuda")
     rows, krows = rows_of(blocks), kv_rows_of(blocks)
     ro, rl = oracle.attn_rows(q, k, v, scale, rows=rows, docs=docs)
+    ra, _ = oracle.attn_rows(q, k, np.abs(v), scale, rows=rows, docs=docs)  # error magnitudes of O
     outs = {}
     for mode in (dfa.DFA_FWD_FUSED, dfa.DFA_FWD_STEPWISE):
         o, lse = dfa.dfa_attn_fwd(tq, tk, tv, blocks, mode, docs=td)
         torch.cuda.synchronize()
         go, gl = bhnd(to_np(o)), to_np(lse)
-        check_out(go[:, :, rows], ro, gl[:, :, rows], rl, dtype, f"mode {mode}")
+        check_out(go[:, :, rows], ro, gl[:, :, rows], rl, dtype, f"mode {mode}", oabs=ra, n_keys=N)
         other = np.setdiff1d(np.arange(N), rows)
         assert np.all(go[:, :, other] == 0) and np.all(np.isneginf(gl[:, :, other]))
         outs[mode] = (o, lse)
@@ -213,7 +215,8 @@ def test_document_mask_parity(dfa, case, dtype):
         op, lp = dfa.dfa_attn_block_fwd(tq, tk, tv, b, docs=td)
         torch.cuda.synchronize()
         xo, xl = oracle.block_partial(q, k, v, 1 / np.sqrt(D), *b[3:8], run=b[10], docs=docs)
-        check_out(to_np(op), xo, to_np(lp), xl, dtype, f"block {b[:3]}")
+        xa, _ = oracle.block_partial(q, k, np.abs(v), 1 / np.sqrt(D), *b[3:8], run=b[10], docs=docs)
+        check_out(to_np(op), xo, to_np(lp), xl, dtype, f"block {b[:3]}", oabs=xa, n_keys=N)
     check_schedule(dfa, blocks, seed, N, B, Hq, Hkv, D, dtype, docs=docs)
 
 
@@ -229,7 +232,8 @@ def test_block_partials_bf16_with_empty_rows(dfa):
         op, lp = dfa.dfa_attn_block_fwd(tq, tk, tv, b)
         torch.cuda.synchronize()
         xo, xl = oracle.block_partial(q, k, v, scale, *b[3:8])
-        check_out(to_np(op), xo, to_np(lp), xl, "bf16", f"block {b[:3]}")
+        xa, _ = oracle.block_partial(q, k, np.abs(v), scale, *b[3:8])
+        check_out(to_np(op), xo, to_np(lp), xl, "bf16", f"block {b[:3]}", oabs=xa, n_keys=N)
         if b[2] > b[0]:
             assert np.all(np.isneginf(to_np(lp)[:, :, 0]))
 
@@ -308,7 +312,8 @@ def test_empty_block_list_and_tiny_sequences(dfa):
         torch.cuda.synchronize()
         scale = 1 / np.sqrt(128)
         ro, rl = oracle.attn_rows(q, k, v, scale)
-        check_out(bhnd(to_np(o)), ro, to_np(lse), rl, "bf16", f"tiny {kind} {N} {P}")
+        ra, _ = oracle.attn_rows(q, k, np.abs(v), scale)
+        check_out(bhnd(to_np(o)), ro, to_np(lse), rl, "bf16", f"tiny {kind} {N} {P}", oabs=ra, n_keys=N)
         (rdq, rdk, rdv), (a1, a2, a3) = oracle.attn_grads(q, k, v, do, scale, with_abs=True)
         # the elementwise bound only: on 1-8 tokens the mean error over a few
         # hundred elements follows which roundings happen -- an emulation of
@@ -355,7 +360,8 @@ def test_strided_views(dfa):
     torch.cuda.synchronize()
     scale = 1 / np.sqrt(D)
     ro, rl = oracle.attn_rows(q, k, v, scale)
-    check_out(bhnd(to_np(o)), ro, to_np(lse), rl, "bf16", "strided")
+    ra, _ = oracle.attn_rows(q, k, np.abs(v), scale)
+    check_out(bhnd(to_np(o)), ro, to_np(lse), rl, "bf16", "strided", oabs=ra, n_keys=N)
     (rdq, rdk, rdv), (a1, a2, a3) = oracle.attn_grads(q, k, v, do, scale, with_abs=True)
     check_grad(bhnd(to_np(dq)), rdq, a1, "bf16", "dq")
     check_grad(bhnd(to_np(dk)), rdk, a2, "bf16", "dk")

@@ -88,9 +88,10 @@ def test_workload_sampled_parity(dfa, name):
         qh, doh = q[:, :, heads], do[:, :, heads]
         kh, vh = k[:, :, [hk]], v[:, :, [hk]]
         ro, rl = oracle.attn_rows(qh, kh, vh, scale, rows=rows, docs=docs)
+        ra, _ = oracle.attn_rows(qh, kh, np.abs(vh), scale, rows=rows, docs=docs)  # error magnitudes of O
         go = bhnd(to_np(o[:, rows][:, :, heads]))
         gl = to_np(lse[:, heads][:, :, rows])
-        check_out(go, ro, gl, rl, "bf16", f"{name} O")
+        check_out(go, ro, gl, rl, "bf16", f"{name} O", oabs=ra, n_keys=N)
         lse_r, dd_r, rdq, aa, adq = oracle.grad_rows(qh, kh, vh, doh, scale, rows=rows, with_abs=True,
                                                      docs=docs)
         gq = bhnd(to_np(dq[:, rows][:, :, heads]))
@@ -229,6 +230,7 @@ def test_stepwise_forward_full_shape(dfa, name):
         heads = list(range(hk * group, (hk + 1) * group))
         print(f"case: stepwise {name} oracle, kv head {hk}, {rows.size} rows", flush=True)
         ro, rl = oracle.attn_rows(q[:, :, heads], k[:, :, [hk]], v[:, :, [hk]], scale, rows=rows)
+        ra, _ = oracle.attn_rows(q[:, :, heads], k[:, :, [hk]], np.abs(v[:, :, [hk]]), scale, rows=rows)
         check_out(bhnd(to_np(o[:, rows][:, :, heads])), ro, to_np(lse[:, heads][:, :, rows]), rl, "bf16",
-                  f"stepwise {name} O")
+                  f"stepwise {name} O", oabs=ra, n_keys=N)
     print(f"case: stepwise {name} done", flush=True)

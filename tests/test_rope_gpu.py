@@ -102,7 +102,8 @@ def test_attention_over_rotated_inputs(dfa):
     # the oracle rotates and stores (bf16) on its own side
     oq, ok = oracle.round_bf16(oracle.rope(q)), oracle.round_bf16(oracle.rope(k))
     ro, rl = oracle.attn_rows(oq, ok, v, scale)
-    check_out(bhnd(to_np(o)), ro, to_np(lse), rl, "bf16", "O")
+    ra, _ = oracle.attn_rows(oq, ok, np.abs(v), scale)
+    check_out(bhnd(to_np(o)), ro, to_np(lse), rl, "bf16", "O", oabs=ra, n_keys=N)
     (gq, gk, gv), (aq, ak, av) = oracle.attn_grads(oq, ok, v, do, scale, with_abs=True)
     # back through the transpose rotation; a rotated element mixes the pair,
     # so its error magnitude is the pair's sum

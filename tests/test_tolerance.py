@@ -244,3 +244,31 @@ def test_unit_roundoff_of_bf16_sets_the_elementwise_bound():
     new = float((e / (G_MAX * rms + G_REL * a)).max())
     print(f"rank-0 share dV: emulated error / (2e-2 rms + 2^-8 g_abs) {old:.3f}, with 2^-7: {new:.3f}")
     assert old > 1.2 and new < 0.7
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,seed,scaled", [(1024, 2, 1, 1003, True), (2048, 2, 2, 1005, False)])
+def test_output_elementwise_bound_under_emulation(N, Hq, Hkv, seed, scaled):
+    """The forward output's elementwise bound of the GPU tests
+    (parity_util.o_bound_ratio: (2^-7 + 2^-12 + gamma) sum_j P_ij |v_j|)
+    holds for the emulated roundings (every probability entering P.V and
+    the stored output rounded to bf16) with margin, and fails for an output
+    off by a relative 2^-6 -- the check sees errors far below the absolute
+    2e-2 bound when the inputs are scaled by 1/sqrt(d)."""
+    from tests.parity_util import o_bound_ratio
+    from tests.bf16_emulation import _mask
+    q, k, v, _ = workload_inputs(N, Hq, Hkv, seed, scaled)
+    scale = 1 / math.sqrt(128)
+    q, k, v = (np.asarray(t, np.float64) for t in (q, k, v))
+    M = _mask(N)
+    for h in range(Hq):
+        hk = h // (Hq // Hkv)
+        S = np.where(M, scale * q[0, :, h] @ k[0, :, hk].T, -np.inf)
+        E = np.exp(S - S.max(axis=1, keepdims=True))
+        ell = E.sum(axis=1, keepdims=True)
+        exact = (E @ v[0, :, hk]) / ell
+        emul = round_bf16((round_bf16(E) @ v[0, :, hk]) / ell)
+        oabs = (E @ np.abs(v[0, :, hk])) / ell
+        ratio = o_bound_ratio(emul, exact, oabs, N)
+        print(f"N={N} head {h}: emulated output bound ratio {ratio:.3f}, max |dO| {np.abs(emul - exact).max():.2e}")
+        assert ratio <= 0.8
+        assert o_bound_ratio(exact * (1 + 2.0 ** -6), exact, oabs, N) > 1.0
