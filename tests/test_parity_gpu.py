@@ -398,3 +398,47 @@ def test_all_heads_at_workload_shapes(dfa, case):
     arrays = inputs.workload_tensors(5000 + P, 1, N, Hq, Hkv, D, "bf16", 1 / np.sqrt(D) if scaled else None,
                                      with_do=True)
     check_schedule(dfa, blocks, None, N, 1, Hq, Hkv, D, "bf16", arrays=arrays)
+
+
+def random_cases(seed=7070, count=40):
+    """Seeded random schedules: kind, ranks, length (a multiple of what the
+    kind needs, ragged against the 64/256-row tiles), batch, heads, head_dim,
+    dtype, a random non-empty set of whole ranks (each rank's blocks cover
+    its rows completely) and sometimes packed documents."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        kind = int(rng.choice([RING, BAL, STR, sr.STRIPED_BLOCK]))
+        P = int(rng.integers(1, 13))
+        stripe = int(rng.choice([64, 128])) if kind == sr.STRIPED_BLOCK else 1
+        unit = {BAL: 2 * P, sr.STRIPED_BLOCK: P * stripe}.get(kind, P)
+        N = unit * int(rng.integers(max(1, 96 // unit), max(2, 1600 // unit) + 1))
+        Hq, Hkv = [(1, 1), (2, 1), (4, 2), (3, 3), (4, 1)][int(rng.integers(0, 5))]
+        B = int(rng.integers(1, 3))
+        D = int(rng.choice([64, 128]))
+        dtype = "f32" if rng.random() < 0.3 else "bf16"
+        ranks = sorted(int(r) for r in rng.choice(P, size=int(rng.integers(1, P + 1)), replace=False))
+        docs = None
+        if rng.random() < 0.35:
+            lo = int(rng.integers(1, 200))
+            docs = (lo, lo + int(rng.integers(0, 600)))
+        out.append(pytest.param((kind, N, P, stripe, B, Hq, Hkv, D, dtype, ranks, docs, 7000 + i),
+                                id=f"r{i}-{sr.KIND_NAMES[kind]}-N{N}-P{P}-{dtype}"))
+    return out
+
+
+@pytest.mark.parametrize("case", random_cases())
+def test_random_schedules(dfa, case):
+    """Parity on seeded random schedules, rank sets, shapes and dtypes (fused
+    and stepwise forward, backward, untouched rows zero)."""
+    from long_context_sequence_dfa_amd import inputs
+    kind, N, P, stripe, B, Hq, Hkv, D, dtype, ranks, doclens, seed = case
+    docs = None if doclens is None else inputs.doc_bounds(seed, N, *doclens)
+    say(f"case: random {sr.KIND_NAMES[kind]} N={N} P={P} stripe={stripe} B={B} Hq={Hq} Hkv={Hkv} D={D} "
+        f"{dtype} ranks={ranks} docs={None if docs is None else len(docs) - 1}")
+    if kind == sr.STRIPED_BLOCK:
+        blocks = dfa.dfa_schedule_build_striped_blocks(N, P, stripe)
+    else:
+        blocks = dfa.dfa_schedule_build(kind, N, P)
+    blocks = blocks[np.isin(blocks[:, 0], ranks)]
+    check_schedule(dfa, blocks, seed, N, B, Hq, Hkv, D, dtype, docs=docs)
