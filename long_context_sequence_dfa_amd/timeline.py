@@ -54,12 +54,13 @@ class HipEvents:
         return float(ms.value)
 
 
-def slot_times(q, k, v, blocks, n_ranks: int, stream=None, docs=None, warmup: int = 1):
-    """Milliseconds per (rank, step) slot, shape [n_ranks, n_ranks], from one
-    ring-faithful stepwise forward (after ``warmup`` untimed ones): slot (r, s)
-    is the time between the events recorded right before its launches and
-    right before the next slot's.  Slots without blocks cost only the gap
-    between two event records."""
+def slot_times(q, k, v, blocks, n_ranks: int, stream=None, docs=None, warmup: int = 1, runs: int = 5):
+    """Milliseconds per (rank, step) slot, shape [n_ranks, n_ranks]: the
+    median over ``runs`` ring-faithful stepwise forwards (after ``warmup``
+    untimed ones) of the time between the events recorded right before the
+    slot's launches and right before the next slot's.  The median per slot
+    keeps launch and clock jitter out of the per-step maxima; slots without
+    blocks cost only the gap between two event records."""
     import torch
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -72,15 +73,18 @@ def slot_times(q, k, v, blocks, n_ranks: int, stream=None, docs=None, warmup: in
         desc = binding.make_desc(q, k, v, o, docs=docs)
         ws = torch.empty(max(binding.dfa_workspace_size(desc, blocks, binding.DFA_OP_FWD_STEPWISE), 256),
                          dtype=torch.uint8, device=q.device)
-        for _ in range(max(warmup, 0) + 1):
+        for _ in range(max(warmup, 0)):
             binding.dfa_attn_fwd_slots(q, k, v, blocks, ev, P, o=o, lse=lse, workspace=ws,
                                        stream=stream, docs=docs)
-        times = np.zeros((P, P), dtype=np.float64)
-        for s in range(P):
-            for r in range(P):
-                i = s * P + r
-                times[r, s] = hip.elapsed(ev[i], ev[i + 1])
-        return times
+        samples = np.zeros((max(int(runs), 1), P, P), dtype=np.float64)
+        for n in range(samples.shape[0]):
+            binding.dfa_attn_fwd_slots(q, k, v, blocks, ev, P, o=o, lse=lse, workspace=ws,
+                                       stream=stream, docs=docs)
+            for s in range(P):
+                for r in range(P):
+                    i = s * P + r
+                    samples[n, r, s] = hip.elapsed(ev[i], ev[i + 1])
+        return np.median(samples, axis=0)
     finally:
         torch.cuda.synchronize()
         for e in ev:
