@@ -1,6 +1,6 @@
 """Measured per-virtual-rank timeline of one forward pass.
 
-The pages judge a schedule by how long each rank computes at each ring step:
+The pages assess a schedule by how long each rank computes at each ring step:
 a step lasts as long as its slowest rank, and the time the other ranks wait
 is the idle bubble (DistFlashAttn Guide, "Breakdown of Idle Time and Bubble
 Elimination"; Striped Attention Guide, "Why Striping Solves Load Imbalance"
