@@ -199,7 +199,7 @@ dfa_status dfa_schedule_build(int32_t kind, int64_t seqlen, int32_t n_ranks, dfa
  * Formulation of Token Striping", block-striped variant, and its "Block
  * Stripe Size" recommendation of 64 or 128).  At step s rank r holds the keys
  * of rank (r - s) mod P, as in DFA_SCHED_STRIPED.  Blocks have run = stripe and
- * stride = P * stride; stripe = 1 reproduces DFA_SCHED_STRIPED exactly.
+ * stride = P * stripe; stripe = 1 reproduces DFA_SCHED_STRIPED exactly.
  *   seqlen : N with N % (n_ranks * stripe) == 0, else DFA_E_SHAPE.
  *   stripe : >= 1.  The attention calls take run = 1 or run = 64 * 2^k (their
  *            row tiles are 64 rows, and a tile's run is found by a shift);
