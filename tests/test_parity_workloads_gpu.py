@@ -31,7 +31,10 @@ WORKLOADS = {
     "llama7b-n32k-striped64-p8": (32768, 32, 32, sr.STRIPED_BLOCK, 8, 1003, True, None, [9]),
     # packed documents of 1K-8K tokens over the folded schedule
     "llama7b-n32k-docs-balanced-p8": (32768, 32, 32, sr.BALANCED, 8, 1003, True, None, [4]),
+    # head_dim 64 (its own tile pitch and load split) over a long folded walk
+    "d64-n64k-balanced-p8": (65536, 16, 16, sr.BALANCED, 8, 1006, False, None, [3]),
 }
+HEAD_DIM = {"d64-n64k-balanced-p8": 64}
 STRIPE = {"llama7b-n32k-striped64-p8": 64}
 DOCS = {"llama7b-n32k-docs-balanced-p8": (1024, 8192)}
 
@@ -50,7 +53,7 @@ def dfa():
 def test_workload_sampled_parity(dfa, name):
     from long_context_sequence_dfa_amd import inputs
     N, Hq, Hkv, kind, P, seed, scaled, rank, kv_heads = WORKLOADS[name]
-    D, group = 128, Hq // Hkv
+    D, group = HEAD_DIM.get(name, 128), Hq // Hkv
     print(f"case: {name} generating inputs", flush=True)
     qs = 1 / math.sqrt(D) if scaled else None
     q, k, v, do = inputs.workload_tensors(seed, 1, N, Hq, Hkv, D, "bf16", qs, with_do=True)
